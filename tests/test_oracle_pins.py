@@ -1,0 +1,542 @@
+"""Pins of the CPU oracle against what the mathematics fixes.
+
+Each test ties one oracle function to something other than itself: a format
+definition checked over every bit pattern against numpy, an exact rational
+computation with Python integers / Fractions, brute force over all subsets,
+closed forms and special cases that reduce to a textbook routine.  The
+comments say which plausible mistake each pin catches.
+"""
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from quantized_expert_ffn_topk_amd import synth
+
+
+# ---------------------------------------------------------------------------
+# format conversions
+# ---------------------------------------------------------------------------
+def test_f16_every_bit_pattern_matches_numpy(orc):
+    # numpy's float16 is an independent implementation of IEEE binary16;
+    # catches a wrong bias, a lost subnormal branch or a shifted fraction.
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float32)
+    got = np.array([orc.f16_to_f32(b) for b in bits], dtype=np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_bf16_to_f32_is_upper_half(orc):
+    for b in [0x0000, 0x8000, 0x3F80, 0xC000, 0x0001, 0x7F7F, 0x7F80, 0xFF80]:
+        want = np.array([b << 16], np.uint32).view(np.float32)[0]
+        assert np.float32(orc.bf16_to_f32(b)).view(np.uint32) == np.float32(want).view(np.uint32)
+
+
+@pytest.mark.parametrize("f32bits,bf16", [
+    (0x3F808000, 0x3F80),   # exact tie, even stays
+    (0x3F818000, 0x3F82),   # exact tie, odd rounds up to even
+    (0x3F808001, 0x3F81),   # just above the tie
+    (0x3F807FFF, 0x3F80),   # just below the tie
+    (0x7F7FFFFF, 0x7F80),   # overflow rounds to +inf
+    (0x7F800000, 0x7F80),   # inf stays inf
+    (0x80000000, 0x8000),   # -0
+    (0x7FA00000, 0x7FE0),   # signalling NaN made quiet
+])
+def test_f32_to_bf16_rne(orc, f32bits, bf16):
+    f = np.array([f32bits], np.uint32).view(np.float32)[0]
+    assert orc.f32_to_bf16(f) == bf16
+
+
+def test_e2m1_table_and_e8m0(orc):
+    # OCP Microscaling v1.0: E2M1 magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}.
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for c in range(16):
+        v = orc.e2m1_value(c)
+        assert abs(v) == mags[c & 7]
+        assert math.copysign(1.0, v) == (-1.0 if c & 8 else 1.0)
+    assert orc.e8m0_value(127) == 1.0
+    assert orc.e8m0_value(0) == 2.0 ** -127
+    assert orc.e8m0_value(254) == 2.0 ** 127
+    assert math.isnan(orc.e8m0_value(255))
+
+
+# ---------------------------------------------------------------------------
+# activation quantisation
+# ---------------------------------------------------------------------------
+def test_quant_worked_example(orc):
+    # amax = 2 -> multiplier 63.5: 1.0 -> 63.5 ties to even 64; -2 -> -127;
+    # 0.5 -> 31.75 -> 32; scale = 2/127.
+    q, s = orc.quant_row(np.array([1.0, -2.0, 0.5, 0.0], np.float32))
+    assert q.tolist() == [64, -127, 32, 0]
+    assert np.float32(s) == np.float32(2.0) / np.float32(127.0)
+
+
+def test_quant_zero_row(orc):
+    q, s = orc.quant_row(np.zeros(64, np.float32))
+    assert not q.any() and s == 0.0
+
+
+def test_quant_error_bound_and_extremes(orc):
+    r = np.random.default_rng(1)
+    for trial in range(50):
+        K = int(r.integers(1, 300))
+        v = (r.standard_normal(K) * 10.0 ** r.uniform(-6, 6)).astype(np.float32)
+        q, s = orc.quant_row(v)
+        amax = np.abs(v).max()
+        # exact rational quotient 127 v / amax: the fp32 decision can only
+        # differ from round-to-nearest by one step right at a tie
+        for i in range(K):
+            exact = Fraction(float(v[i])) * 127 / Fraction(float(amax))
+            assert abs(Fraction(int(q[i])) - exact) <= Fraction(1, 2) + Fraction(1, 10**5)
+        j = int(np.argmax(np.abs(v)))
+        assert abs(int(q[j])) == 127 and np.sign(q[j]) == np.sign(v[j])
+        assert np.all(np.abs(q.astype(int)) <= 127)
+        # reconstruction within half a step (plus rounding of s itself)
+        err = np.abs(v.astype(np.float64) - q.astype(np.float64) * s)
+        assert np.all(err <= 0.5 * s * (1 + 1e-6) + 1e-30)
+
+
+# ---------------------------------------------------------------------------
+# router
+# ---------------------------------------------------------------------------
+def _exact_logits(x_bf16, Wr):
+    xf = synth.bf16_bits_to_f32(x_bf16)
+    T, H = xf.shape
+    E = Wr.shape[0]
+    L = np.empty((T, E))
+    for t in range(T):
+        xs = [Fraction(float(v)) for v in xf[t]]
+        for e in range(E):
+            L[t, e] = float(sum(a * Fraction(float(w)) for a, w in zip(xs, Wr[e])))
+    return L
+
+
+def test_router_bruteforce_tiny(orc):
+    # All k-subsets of E experts: the selected set must maximise sum(c) and the
+    # rank order must be c descending.  Logits from exact rationals.
+    r = np.random.default_rng(7)
+    for trial in range(25):
+        E = int(r.integers(3, 11))
+        k = int(r.integers(1, min(E, 6) + 1))
+        H, T = 32, 3
+        x = synth.f32_to_bf16_bits(r.standard_normal((T, H)).astype(np.float32))
+        Wr = (r.standard_normal((E, H)) * 0.2).astype(np.float32)
+        b = (r.standard_normal(E) * 0.05).astype(np.float32)
+        rs = float(r.uniform(0.5, 3.0))
+        idx, w = orc.router(x, Wr, b, k, rs)
+        L = _exact_logits(x, Wr)
+        for t in range(T):
+            s = [1.0 / (1.0 + math.exp(-L[t, e])) for e in range(E)]
+            c = [s[e] + float(b[e]) for e in range(E)]
+            best = max(itertools.combinations(range(E), k), key=lambda S: sum(c[e] for e in S))
+            assert set(idx[t].tolist()) == set(best)
+            order = sorted(best, key=lambda e: (-c[e], e))
+            assert idx[t].tolist() == order
+            den = sum(s[e] for e in order)
+            for i, e in enumerate(order):
+                assert abs(w[t, i] - s[e] / den * rs) <= 1e-6 * rs
+
+
+def test_router_one_hot_input_reads_the_right_weight(orc):
+    # x = unit vector at column j -> logit of expert e is exactly Wr[e, j];
+    # a transposed weight read (Wr[j, e]) or a wrong row stride fails this.
+    E, H, k = 8, 16, 3
+    r = np.random.default_rng(3)
+    Wr = r.standard_normal((E, H)).astype(np.float32)
+    for j in [0, 5, 15]:
+        xf = np.zeros((1, H), np.float32)
+        xf[0, j] = 1.0
+        x = synth.f32_to_bf16_bits(xf)
+        _, _, lg, sc, ch = orc.router(x, Wr, np.zeros(E, np.float32), k, 1.0, want=True)
+        assert np.array_equal(lg[0], Wr[:, j].astype(np.float64))
+        want = np.argsort(-Wr[:, j], kind="stable")[:k]
+        idx, _ = orc.router(x, Wr, np.zeros(E, np.float32), k, 1.0)
+        assert idx[0].tolist() == want.tolist()
+
+
+def test_router_sigmoid_zero_and_ties(orc):
+    # Zero weights: every logit 0, sigmoid(0) = 0.5 exactly, all c tied ->
+    # lowest indices in order, equal weights r/k.
+    E, H, k, rs = 12, 32, 4, 2.5
+    x = synth.f32_to_bf16_bits(np.ones((2, H), np.float32))
+    idx, w, lg, sc, ch = orc.router(x, np.zeros((E, H), np.float32), np.zeros(E, np.float32),
+                                    k, rs, want=True)
+    assert np.all(sc == 0.5)
+    assert idx.tolist() == [[0, 1, 2, 3]] * 2
+    assert np.allclose(w, rs / k, rtol=0, atol=1e-7)
+    # tied bias on two duplicated rows: the lower index ranks first
+    r = np.random.default_rng(5)
+    Wr = (r.standard_normal((E, H)) * 0.1).astype(np.float32)
+    Wr[9] = Wr[4]
+    b = np.full(E, -1.0, np.float32)
+    b[4] = b[9] = 1.0
+    idx, _ = orc.router(x, Wr, b, 2, 1.0)
+    assert idx.tolist() == [[4, 9]] * 2
+
+
+def test_router_zero_bias_is_topk_of_logits(orc):
+    # sigmoid is monotone, so with b = 0 the choice equals the top-k of the
+    # logits, computed here by numpy's fp64 matmul.
+    r = np.random.default_rng(11)
+    T, E, H, k = 20, 64, 256, 8
+    x = synth.f32_to_bf16_bits(r.standard_normal((T, H)).astype(np.float32))
+    Wr = (r.standard_normal((E, H)) * 0.05).astype(np.float32)
+    idx, _ = orc.router(x, Wr, np.zeros(E, np.float32), k, 1.0)
+    L = synth.bf16_bits_to_f32(x).astype(np.float64) @ Wr.astype(np.float64).T
+    for t in range(T):
+        o = np.argsort(-L[t], kind="stable")
+        gaps = np.abs(np.diff(np.sort(L[t])[::-1][:k + 1]))
+        assert gaps.min() > 1e-9
+        assert idx[t].tolist() == o[:k].tolist()
+
+
+def test_router_weights_ignore_bias(orc):
+    # The bias steers selection only: with a big bias forcing a set, the
+    # weights are the normalised sigmoid scores and sum to r.
+    r = np.random.default_rng(13)
+    T, E, H, k, rs = 4, 16, 64, 4, 2.5
+    x = synth.f32_to_bf16_bits(r.standard_normal((T, H)).astype(np.float32))
+    Wr = (r.standard_normal((E, H)) * 0.1).astype(np.float32)
+    forced = [3, 7, 11, 12]
+    b = synth.forcing_bias(E, forced)
+    idx, w, lg, sc, ch = orc.router(x, Wr, b, k, rs, want=True)
+    for t in range(T):
+        assert sorted(idx[t].tolist()) == forced
+        s = sc[t, idx[t]]
+        assert np.allclose(w[t], s / s.sum() * rs, rtol=1e-6, atol=0)
+        assert abs(float(w[t].astype(np.float64).sum()) - rs) <= 1e-6 * rs
+        assert np.all(np.diff(s) <= 0)            # rank order is by c = s + 4
+
+
+# ---------------------------------------------------------------------------
+# int4 x int8 projection
+# ---------------------------------------------------------------------------
+def _rand_i4(r, N, K, g, scale_exp_spread=3):
+    qw = r.integers(-8, 8, size=(N, K)).astype(np.int8)
+    e = r.integers(-9, -9 + scale_exp_spread, size=(N, K // g))
+    m = r.uniform(1.0, 2.0, size=(N, K // g))
+    S = np.ldexp(m, e).astype(np.float16).view(np.uint16)
+    return qw, S
+
+
+def test_group_dots_match_int64(orc):
+    r = np.random.default_rng(17)
+    for g in (32, 64):
+        N, K = 24, 256
+        qw, _ = _rand_i4(r, N, K, g)
+        q = r.integers(-127, 128, size=K).astype(np.int8)
+        acc = orc.group_dots(q, qw, g)
+        ref = (qw.astype(np.int64).reshape(N, K // g, g) * q.astype(np.int64).reshape(K // g, g)).sum(-1)
+        assert np.array_equal(acc, ref)
+
+
+def test_proj_unit_scales_equal_integer_brute_force(orc):
+    # S = 1 and s_in = 1: the output is an integer below 2^24, so it must equal
+    # the int64 matmul exactly (pins the int32 accumulators end to end).
+    r = np.random.default_rng(19)
+    N, K, g = 40, 512, 32
+    qw = r.integers(-8, 8, size=(N, K)).astype(np.int8)
+    S = np.full((N, K // g), 0x3C00, np.uint16)          # fp16 1.0
+    q = r.integers(-127, 128, size=K).astype(np.int8)
+    y = orc.proj_i4i8(q, 1.0, qw, S, g)
+    ref = qw.astype(np.int64) @ q.astype(np.int64)
+    assert np.array_equal(y.astype(np.int64), ref)
+    assert np.all(np.abs(ref) < 2 ** 24)
+
+
+def test_proj_equals_exact_rational_rounded(orc):
+    # With real fp16 scales the result is fp32(fp64(exact sum) * s_in); the
+    # exact sum is computed here with Python integers and Fractions.
+    r = np.random.default_rng(23)
+    N, K, g = 16, 384, 32
+    qw, S = _rand_i4(r, N, K, g)
+    q = r.integers(-127, 128, size=K).astype(np.int8)
+    s_in = np.float32(r.uniform(0.001, 0.1))
+    y = orc.proj_i4i8(q, s_in, qw, S, g)
+    Sf = S.view(np.float16).astype(np.float64)
+    for n in range(N):
+        exact = Fraction(0)
+        for j in range(K // g):
+            a = int(np.dot(qw[n, j * g:(j + 1) * g].astype(np.int64), q[j * g:(j + 1) * g].astype(np.int64)))
+            exact += a * Fraction(float(Sf[n, j]))
+        want = np.float32(float(Fraction(float(exact)) * Fraction(float(s_in))))
+        assert float(exact) == exact           # the fp64 sum is exact
+        assert y[n].view(np.uint32) == want.view(np.uint32)
+
+
+def test_proj_equals_dequantised_float_matmul(orc):
+    # int4 x int8 equals the dequantised float matmul (q_w*S) @ (q*s_in).
+    r = np.random.default_rng(29)
+    N, K, g = 64, 1024, 32
+    qw, S = _rand_i4(r, N, K, g)
+    q = r.integers(-127, 128, size=K).astype(np.int8)
+    s_in = np.float32(0.0123)
+    y = orc.proj_i4i8(q, s_in, qw, S, g)
+    Wd = qw.astype(np.float64) * np.repeat(S.view(np.float16).astype(np.float64), g, axis=1)
+    ref = Wd @ (q.astype(np.float64) * float(s_in))
+    assert np.allclose(y, ref, rtol=2 ** -23, atol=1e-30)
+
+
+def test_proj_row_and_group_indexing(orc):
+    # One nonzero weight at (n0, k0) and powers-of-two scales per group: only
+    # row n0 responds, with the scale of group k0 // g.  A transposed weight
+    # or a scale indexed by the wrong group fails this.
+    N, K, g = 8, 128, 32
+    qw = np.zeros((N, K), np.int8)
+    n0, k0 = 5, 77
+    qw[n0, k0] = 3
+    S = np.zeros((N, K // g), np.float16)
+    for j in range(K // g):
+        S[:, j] = 2.0 ** j
+    q = np.zeros(K, np.int8)
+    q[k0] = -7
+    y = orc.proj_i4i8(q, 1.0, qw, S.view(np.uint16), g)
+    want = np.zeros(N, np.float32)
+    want[n0] = 3 * -7 * 2.0 ** (k0 // g)
+    assert np.array_equal(y, want)
+    rows = np.array([n0, 0], np.int32)
+    assert np.array_equal(orc.proj_i4i8(q, 1.0, qw, S.view(np.uint16), g, rows=rows), want[[n0, 0]])
+
+
+def test_rows_exact_fp64_bound(orc):
+    N, K, g = 2, 256, 32
+    S = np.full((N, K // g), np.float16(0.01)).view(np.uint16)
+    assert orc.rows_exact_fp64(S, K, g)
+    S2 = S.copy().view(np.float16)
+    S2[1, 0] = np.float16(6e-8)        # subnormal next to ~2^-7: spread 17 binades
+    S2[1, 1] = np.float16(60000.0)     # spread ~40 binades -> not exact
+    assert not orc.rows_exact_fp64(S2.view(np.uint16), K, g)
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU expert
+# ---------------------------------------------------------------------------
+def _expert(seed, H, F, g, e=0):
+    return synth.expert_int4(seed, e, H, F, g)
+
+
+def test_expert_zero_gate_gives_zero(orc):
+    # silu(0) = 0: zero gate rows -> h = 0 -> zero requant -> y = 0.
+    H, F, g = 256, 128, 32
+    ex = _expert(0, H, F, g)
+    ex["q_gate"] = np.zeros_like(ex["q_gate"])
+    r = np.random.default_rng(31)
+    qa = r.integers(-127, 128, size=H).astype(np.int8)
+    res = orc.expert(qa, 0.01, ex, g)
+    assert not res["h"].any() and not res["qh"].any() and res["sh"] == 0.0
+    assert not res["y"].any()
+
+
+def test_expert_silu_limits(orc):
+    # Gate rows equal to up rows scaled up: G = c*U with |G| large.  For
+    # G >> 0 silu(G) = G, so h = G*U; for G << 0 silu(G)*U is ~0.
+    H, F, g = 256, 64, 32
+    r = np.random.default_rng(37)
+    qa = r.integers(-127, 128, size=H).astype(np.int8)
+    sa = np.float32(1.0)
+    q = r.integers(-8, 8, size=(F, H)).astype(np.int8)
+    S = np.full((F, H // g), 0x3C00, np.uint16)                 # 1.0
+    ex = dict(q_gate=q, s_gate=S, q_up=q, s_up=S,
+              q_down=np.zeros((H, F), np.int8), s_down=np.zeros((H, F // g), np.uint16))
+    res = orc.expert(qa, sa, ex, g)
+    G = (q.astype(np.int64) @ qa.astype(np.int64)).astype(np.float64)
+    big = np.abs(G) > 60
+    assert big.any()
+    pos = big & (G > 0)
+    neg = big & (G < 0)
+    assert np.array_equal(res["h"][pos], (G[pos] * G[pos]).astype(np.float32))
+    assert np.all(np.abs(res["h"][neg]) < 1e-20)
+    # G = 0 rows give exactly 0
+    assert np.all(res["h"][G == 0] == 0.0)
+
+
+def test_expert_requant_and_down_consistent(orc):
+    # The down projection consumes exactly the requantised h: recompute it with
+    # proj_i4i8 on the returned (qh, sh) and with the integer brute force.
+    H, F, g = 256, 128, 32
+    ex = _expert(1, H, F, g)
+    r = np.random.default_rng(41)
+    xf = r.standard_normal(H).astype(np.float32)
+    qa, sa = orc.quant_row(xf)
+    res = orc.expert(qa, sa, ex, g)
+    qh2, sh2 = orc.quant_row(res["h"])
+    assert np.array_equal(qh2, res["qh"]) and sh2 == res["sh"]
+    y2 = orc.proj_i4i8(res["qh"], res["sh"], ex["q_down"], ex["s_down"], g)
+    assert np.array_equal(y2, res["y"])
+    # h against an fp64 dequantised computation of the gate/up products
+    Wg = ex["q_gate"].astype(np.float64) * np.repeat(ex["s_gate"].view(np.float16).astype(np.float64), g, 1)
+    Wu = ex["q_up"].astype(np.float64) * np.repeat(ex["s_up"].view(np.float16).astype(np.float64), g, 1)
+    a = qa.astype(np.float64) * float(sa)
+    G, U = Wg @ a, Wu @ a
+    h_ref = G / (1.0 + np.exp(-G)) * U
+    assert np.allclose(res["h"], h_ref, rtol=1e-6, atol=1e-12)
+    # sampled rows equal the full output at those rows
+    rows = np.array([255, 3, 128], np.int32)
+    res2 = orc.expert(qa, sa, ex, g, down_rows=rows)
+    assert np.array_equal(res2["y"], res["y"][rows])
+
+
+# ---------------------------------------------------------------------------
+# whole layer
+# ---------------------------------------------------------------------------
+def _layer_inputs(seed, T, H, F, E, g):
+    x = synth.activations(seed, T, H)
+    Wr, b = synth.router_weights(seed, E, H)
+    exps = [synth.expert_int4(seed, e, H, F, g) for e in range(E)]
+    shared = synth.expert_int4(seed, -1, H, F, g)
+    return x, Wr, b, exps, shared
+
+
+def test_layer_single_expert_is_dense_mlp(orc):
+    # E = 1, k = 1, r = 1, no shared expert: the layer is one dense quantised
+    # SwiGLU MLP, i.e. the expert applied to the quantised token.
+    H, F, g, T = 256, 128, 32, 3
+    x, Wr, b, exps, _ = _layer_inputs(2, T, H, F, 1, g)
+    idx, w, out = orc.layer(x, Wr, b, exps, None, 1, 1.0, g)
+    assert np.all(idx == 0) and np.all(w == 1.0)
+    xf = synth.bf16_bits_to_f32(x)
+    for t in range(T):
+        qa, sa = orc.quant_row(xf[t])
+        assert np.array_equal(out[t], orc.expert(qa, sa, exps[0], g)["y"])
+
+
+def test_layer_shared_only_when_scale_zero(orc):
+    # r = 0: every routed weight is 0, the output is exactly the shared expert.
+    H, F, g, T, E = 256, 64, 32, 2, 6
+    x, Wr, b, exps, shared = _layer_inputs(3, T, H, F, E, g)
+    _, w, out = orc.layer(x, Wr, b, exps, shared, 2, 0.0, g)
+    assert not w.any()
+    xf = synth.bf16_bits_to_f32(x)
+    for t in range(T):
+        qa, sa = orc.quant_row(xf[t])
+        assert np.array_equal(out[t], orc.expert(qa, sa, shared, g)["y"])
+
+
+def test_layer_combine_weights(orc):
+    # out = Y_shared + sum_i w_i Y_idx_i, checked against the per-expert
+    # outputs recomputed separately (fp64 sum, one rounding).
+    H, F, g, T, E, k, rs = 256, 64, 32, 4, 8, 3, 2.5
+    x, Wr, b, exps, shared = _layer_inputs(4, T, H, F, E, g)
+    idx, w, out = orc.layer(x, Wr, b, exps, shared, k, rs, g)
+    xf = synth.bf16_bits_to_f32(x)
+    for t in range(T):
+        qa, sa = orc.quant_row(xf[t])
+        acc = orc.expert(qa, sa, shared, g)["y"].astype(np.float64)
+        for i in range(k):
+            acc = acc + float(w[t, i]) * orc.expert(qa, sa, exps[idx[t, i]], g)["y"].astype(np.float64)
+        assert np.array_equal(out[t], acc.astype(np.float32))
+        assert abs(float(w[t].astype(np.float64).sum()) - rs) < 1e-6 * rs
+
+
+def test_layer_expert_permutation_invariance(orc):
+    # Relabelling the experts (router rows, bias and weights together) changes
+    # nothing in the output: catches an idx -> expert indexing mistake.
+    H, F, g, T, E, k = 256, 64, 32, 3, 7, 2
+    x, Wr, b, exps, shared = _layer_inputs(5, T, H, F, E, g)
+    perm = np.array([3, 6, 0, 5, 1, 2, 4])
+    _, _, out1 = orc.layer(x, Wr, b, exps, shared, k, 1.0, g)
+    inv = np.argsort(perm)
+    _, _, out2 = orc.layer(x, Wr[perm], b[perm], [exps[p] for p in perm], shared, k, 1.0, g)
+    assert np.array_equal(out1, out2)
+    idx1, _ = orc.router(x, Wr, b, k, 1.0)
+    idx2, _ = orc.router(x, Wr[perm], b[perm], k, 1.0)
+    assert np.array_equal(perm[idx2], idx1)
+    del inv
+
+
+def test_layer_identical_experts(orc):
+    # All routed experts identical: out = Y_sh + (sum w) * Y = Y_sh + r*Y.
+    H, F, g, T, E, k, rs = 256, 64, 32, 2, 5, 3, 2.5
+    x, Wr, b, exps, shared = _layer_inputs(6, T, H, F, E, g)
+    same = [exps[0]] * E
+    _, _, out = orc.layer(x, Wr, b, same, shared, k, rs, g)
+    xf = synth.bf16_bits_to_f32(x)
+    for t in range(T):
+        qa, sa = orc.quant_row(xf[t])
+        y = orc.expert(qa, sa, exps[0], g)["y"].astype(np.float64)
+        ysh = orc.expert(qa, sa, shared, g)["y"].astype(np.float64)
+        assert np.allclose(out[t], ysh + rs * y, rtol=1e-5, atol=1e-6 * np.abs(y).max())
+
+
+def test_layer_zero_token(orc):
+    # A zero token: amax 0 -> all codes 0 -> output exactly 0; routing falls
+    # back to the bias (every logit 0, sigmoid 0.5).
+    H, F, g, E, k = 256, 64, 32, 8, 3
+    x, Wr, b, exps, shared = _layer_inputs(7, 2, H, F, E, g)
+    x[1] = 0
+    idx, w, out = orc.layer(x, Wr, b, exps, shared, k, 1.0, g)
+    assert not out[1].any()
+    assert idx[1].tolist() == np.argsort(-b, kind="stable")[:k].tolist()
+    assert np.allclose(w[1], 1.0 / k)
+
+
+def test_layer_sampled_rows(orc):
+    H, F, g, T, E, k = 256, 64, 32, 2, 6, 2
+    x, Wr, b, exps, shared = _layer_inputs(8, T, H, F, E, g)
+    _, _, full = orc.layer(x, Wr, b, exps, shared, k, 1.0, g)
+    rows = np.array([7, 200, 0], np.int32)
+    _, _, part = orc.layer(x, Wr, b, exps, shared, k, 1.0, g, out_rows=rows)
+    assert np.array_equal(part, full[:, rows])
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 variant
+# ---------------------------------------------------------------------------
+def test_proj_mx_equals_exact_rational(orc):
+    r = np.random.default_rng(43)
+    N, K = 6, 128
+    codes = r.integers(0, 16, size=(N, K)).astype(np.uint8)
+    e8 = r.integers(120, 131, size=(N, K // 32)).astype(np.uint8)
+    a = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(r.standard_normal(K).astype(np.float32)))
+    y = orc.proj_mx(a, codes, e8)
+    mags = [0, Fraction(1, 2), 1, Fraction(3, 2), 2, 3, 4, 6]
+    for n in range(N):
+        exact = Fraction(0)
+        for j in range(K):
+            c = int(codes[n, j])
+            v = mags[c & 7] * (-1 if c & 8 else 1) * Fraction(2) ** (int(e8[n, j // 32]) - 127)
+            exact += Fraction(float(a[j])) * v
+        assert y[n] == np.float32(float(exact))
+
+
+def test_mx_expert_against_fp64_dequant(orc):
+    H, F = 256, 64
+    ex = synth.expert_mxfp4(0, 0, H, F)
+    r = np.random.default_rng(47)
+    a = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(r.standard_normal(H).astype(np.float32)))
+    res = orc.mx_expert(a, ex)
+
+    def deq(c, e):
+        v = np.array([orc.e2m1_value(i) for i in range(16)], np.float64)[c]
+        return v * np.repeat(np.ldexp(1.0, e.astype(np.int64) - 127), 32, axis=1)
+
+    G = deq(ex["c_gate"], ex["e_gate"]) @ a.astype(np.float64)
+    U = deq(ex["c_up"], ex["e_up"]) @ a.astype(np.float64)
+    h = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits((G / (1 + np.exp(-G)) * U).astype(np.float32)))
+    y = deq(ex["c_down"], ex["e_down"]) @ h.astype(np.float64)
+    hb = synth.bf16_bits_to_f32(res["h_bf16"])
+    # h may differ by one bf16 step where fp32 rounding of G/U lands on a tie
+    assert np.mean(hb == h) > 0.98
+    assert np.allclose(res["y"], y, rtol=1e-2, atol=1e-3 * np.abs(y).max())
+
+
+def test_mx_layer_runs_and_routes(orc):
+    H, F, T, E, k = 256, 64, 3, 6, 2
+    x = synth.activations(9, T, H)
+    Wr, _ = synth.router_weights(9, E, H)
+    b = synth.uniform_bias(9, E)
+    exps = [synth.expert_mxfp4(9, e, H, F) for e in range(E)]
+    shared = synth.expert_mxfp4(9, -1, H, F)
+    idx, w, out = orc.mx_layer(x, Wr, b, exps, shared, k, 1.0)
+    idx2, w2 = orc.router(x, Wr, b, k, 1.0)
+    assert np.array_equal(idx, idx2) and np.array_equal(w, w2)
+    xf = synth.bf16_bits_to_f32(x)
+    for t in range(T):
+        acc = orc.mx_expert(xf[t], shared)["y"].astype(np.float64)
+        for i in range(k):
+            acc = acc + float(w[t, i]) * orc.mx_expert(xf[t], exps[idx[t, i]])["y"].astype(np.float64)
+        assert np.array_equal(out[t], acc.astype(np.float32))
