@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Throughput of one quantised MoE layer on one MI355X.
+
+Default workload (the decode headline): a GLM-shaped MoE layer with hidden
+6144, 256 routed experts + 1 shared expert, FFN 2048 SwiGLU, int4 weights in
+groups of 32 with fp16 scales, top-8 sigmoid router with selection bias
+N(0, 0.01), routed scale 2.5; batch 1 token per step with fresh N(0,1)
+activations every step.  A step is one moe_layer_forward: token quantisation,
+router + top-k, permutation, routed and shared gate/up + SwiGLU, requant, down
+projections and combine.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Prints one JSON line.  `value` is layer tokens/s with all inputs resident in
+HBM; `roofline` covers the dominant kernel (the gate/up projection) timed with
+HIP events inside the real pipeline; `cpu_baseline` is the plain C oracle on a
+bounded sample of the same workload, on this host.
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s (decode bs1, prefill 4096) + % HBM BW / % int8 MFMA peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, datasheet
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, datasheet
+
+H, F, E, K_TOP, G = 6144, 2048, 256, 8, 32
+R_SCALE = 2.5
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gu_section_bytes(H_, F_, g):
+    return F_ * H_ + (F_ // 8) * (H_ // g) * 32          # nibbles + fp16 scales of 2F rows
+
+
+def dn_section_bytes(H_, F_, g):
+    return H_ * F_ // 2 + (H_ // 16) * (F_ // g) * 32
+
+
+def build_layer(args):
+    from quantized_expert_ffn_topk_amd import abi, synth
+    from quantized_expert_ffn_topk_amd.layer import Layer, make_desc
+    t0 = time.time()
+    D = args.distinct
+    distinct = [synth.expert_int4(0, e, H, F, G) for e in range(D)]
+    shared = synth.expert_int4(0, -1, H, F, G)
+    Wr, b = synth.router_weights(0, E, H)
+    desc = make_desc(H, F, E, K_TOP, 1, G, R_SCALE)
+    lay = Layer(desc, Wr, b, distinct, shared, [e % D for e in range(E)], max_tokens=1)
+    log("layer built in %.1f s (%d distinct synthetic experts behind %d device blobs)" % (
+        time.time() - t0, D, E))
+    return lay, dict(distinct=distinct, shared=shared, Wr=Wr, b=b)
+
+
+def run_decode(args, lay):
+    import torch
+    from quantized_expert_ffn_topk_amd import abi, synth
+    n_x = args.warmup + args.steps + args.profile_steps
+    xs_host = synth.activations(1, n_x, H)
+    xs = lay.x_tensor(xs_host)
+    idx = torch.empty((1, K_TOP), dtype=torch.int32, device=lay.dev)
+    w = torch.empty((1, K_TOP), dtype=torch.float32, device=lay.dev)
+    out = torch.empty((1, H), dtype=torch.float32, device=lay.dev)
+    stream = torch.cuda.Stream()
+    outs = (idx, w, out)
+
+    def step(i):
+        lay.forward(xs[i:i + 1], stream=stream, outs=outs)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+    torch.cuda.synchronize()
+
+    base = args.warmup
+    res = {}
+    # eager launches
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(base + i)
+    stream.synchronize()
+    torch.cuda.synchronize()
+    res["eager_s"] = time.perf_counter() - t0
+    # the same steps captured once as a HIP graph and replayed
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(args.steps):
+                step(base + i)
+        g.replay()                       # first replay (untimed)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+        stream.synchronize()
+        torch.cuda.synchronize()
+        res["graph_s"] = time.perf_counter() - t0
+        res["graph_event_s"] = ev0.elapsed_time(ev1) / 1e3
+        del g
+    # per-kernel durations inside the pipeline (HIP events around each launch)
+    abi.moe_ctx_profile(lay.ctx, True)
+    abi.moe_ctx_profile_read(lay.ctx)
+    pbase = args.warmup + args.steps
+    for i in range(args.profile_steps):
+        step(pbase + i)
+    torch.cuda.synchronize()
+    prof = abi.moe_ctx_profile_read(lay.ctx)
+    abi.moe_ctx_profile(lay.ctx, False)
+    res["kernels_us"] = {k: 1e3 * v[0] / v[1] for k, v in prof.items() if v[1]}
+    return res
+
+
+def run_prefill(args, lay):
+    """4096-token prefill through a second context on the same device blobs,
+    with the Zipf(1.1)-skewed selection bias."""
+    import torch
+    from quantized_expert_ffn_topk_amd import abi, synth
+    T = args.prefill_tokens
+    ctx = abi.moe_ctx_create(0, lay.desc, T)
+    bz = torch.from_numpy(synth.zipf_bias(0, E)).to(lay.dev)
+    wts = abi.moe_layer_weights(lay.Wr.data_ptr(), bz.data_ptr(), lay.ptrs.data_ptr(),
+                                lay.shared_blob.data_ptr())
+    xs = [lay.x_tensor(synth.activations(10 + i, T, H)) for i in range(2)]
+    idx = torch.empty((T, K_TOP), dtype=torch.int32, device=lay.dev)
+    w = torch.empty((T, K_TOP), dtype=torch.float32, device=lay.dev)
+    out = torch.empty((T, H), dtype=torch.float32, device=lay.dev)
+    stream = torch.cuda.Stream()
+    sh = abi.stream_handle(stream)
+
+    def call(i):
+        abi.moe_layer_forward(ctx, xs[i % 2], T, wts, None, 0, idx, w, out, sh)
+
+    for i in range(2):
+        call(i)
+    torch.cuda.synchronize()
+    n = args.prefill_calls
+    t0 = time.perf_counter()
+    for i in range(n):
+        call(i)
+    stream.synchronize()
+    dt = (time.perf_counter() - t0) / n
+    abi.moe_ctx_profile(ctx, True)
+    abi.moe_ctx_profile_read(ctx)
+    for i in range(n):
+        call(i)
+    torch.cuda.synchronize()
+    prof = abi.moe_ctx_profile_read(ctx)
+    abi.moe_ctx_profile(ctx, False)
+    loads = np.bincount(idx.cpu().numpy().ravel(), minlength=E)
+    abi.moe_ctx_destroy(ctx)
+    kus = {k: 1e3 * v[0] / v[1] for k, v in prof.items() if v[1]}
+    rows = T * (K_TOP + 1)
+    ops = 2.0 * rows * (2 * F * H + H * F)                 # int8 MFMA operations (2 per MAC)
+    gemm_us = kus.get("gateup", 0.0) + kus.get("down", 0.0)
+    sorted_loads = np.sort(loads)[::-1]
+    return {
+        "workload": "same layer, prefill of %d tokens, selection bias skewing loads like "
+                    "Zipf(1.1)" % T,
+        "tokens_per_s": T / dt,
+        "ms_per_call": 1e3 * dt,
+        "int8_mfma": {"ops_per_call": ops, "gemm_us": gemm_us,
+                      "achieved_TOPS": ops / (gemm_us * 1e-6) / 1e12,
+                      "peak_TOPS": INT8_PEAK_TOPS,
+                      "frac": ops / (gemm_us * 1e-6) / 1e12 / INT8_PEAK_TOPS},
+        "kernels_us": {k: round(v, 2) for k, v in kus.items()},
+        "expert_loads": {"max": int(loads.max()), "empty": int((loads == 0).sum()),
+                         "top8_share": float(sorted_loads[:8].sum() / loads.sum()),
+                         "top32_share": float(sorted_loads[:32].sum() / loads.sum())},
+    }
+
+
+def cpu_baseline(args, lay, W):
+    """The plain C oracle (single thread) on a bounded sample of decode steps."""
+    import oracle
+    from quantized_expert_ffn_topk_amd import synth
+    oracle.lib()
+    xs = synth.activations(2, args.cpu_steps_max, H)
+    emap = [e % args.distinct for e in range(E)]
+    t0 = time.perf_counter()
+    n = 0
+    while n < args.cpu_steps_max:
+        oracle.layer(xs[n:n + 1], W["Wr"], W["b"], W["distinct"], W["shared"], K_TOP, R_SCALE, G,
+                     expert_map=emap)
+        n += 1
+        if time.perf_counter() - t0 > args.cpu_seconds and n >= 2:
+            break
+    dt = time.perf_counter() - t0
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%d decode steps (batch 1) of the same layer, full 6144-wide output, "
+                      "single-threaded C (gcc -O2) on %s; host has %d logical CPUs" % (
+                          n, cpu, os.cpu_count() or 0)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--profile-steps", type=int, default=200)
+    ap.add_argument("--distinct", type=int, default=8,
+                    help="distinct synthetic experts copied into the 256 device blobs")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-steps-max", type=int, default=40)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-tokens", type=int, default=4096)
+    ap.add_argument("--prefill-calls", type=int, default=5)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs as a single process on one GPU", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    lay, W = build_layer(args)
+    res = run_decode(args, lay)
+    K = args.steps
+    best = min(res["eager_s"], res.get("graph_s", 1e30))
+    ms_per_step = 1e3 * best / K
+    gu_bytes = 9 * gu_section_bytes(H, F, G) + H + 9 * F * 4
+    gu_us = res["kernels_us"]["gateup"]
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+    dn_bytes = 9 * dn_section_bytes(H, F, G) + 9 * F + 9 * H * 4
+    dn_us = res["kernels_us"]["down"]
+    line = {
+        "metric": METRIC,
+        "value": K / best,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {
+            "workload": "GLM-shaped MoE layer decode, batch 1: hidden 6144, 256 routed + 1 shared "
+                        "experts, FFN 2048 SwiGLU, int4 group-32 fp16 scales, int8 activations, "
+                        "top-8 sigmoid router with bias N(0,0.01), routed scale 2.5, fresh "
+                        "N(0,1) tokens each step",
+            "global_batch": 1,
+            "timing": "graph replay" if best == res.get("graph_s") else "eager launches",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gateup_gemv (routed + shared gate/up projections + SwiGLU)",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "bytes_per_launch": gu_bytes,
+            "avg_us": gu_us,
+        },
+        "gemv_hbm": {
+            "down_achieved_GBs": dn_bytes / (dn_us * 1e-6) / 1e9,
+            "gateup_plus_down_GBs": (gu_bytes + dn_bytes) / ((gu_us + dn_us) * 1e-6) / 1e9,
+            "frac": (gu_bytes + dn_bytes) / ((gu_us + dn_us) * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        },
+        "kernels_us": {k: round(v, 3) for k, v in res["kernels_us"].items()},
+        "eager_tokens_per_s": K / res["eager_s"],
+        "graph_tokens_per_s": (K / res["graph_s"]) if "graph_s" in res else None,
+    }
+    if not args.no_prefill:
+        line["prefill"] = run_prefill(args, lay)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args, lay, W)
+    else:
+        line["cpu_baseline"] = None
+    line["host"] = platform.node()
+    print(json.dumps(line), flush=True)
+    lay.close()
+
+
+if __name__ == "__main__":
+    main()

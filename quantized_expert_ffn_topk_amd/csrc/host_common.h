@@ -1,0 +1,89 @@
+// host_common.h -- host-side state shared by the C ABI implementation files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <vector>
+
+#include "moe_internal.h"
+
+// Context: descriptor, kernel path and the workspace of one layer shape.
+struct moe_ctx {
+    int device = 0;
+    moe_layer_desc d{};
+    int max_tokens = 0;
+    int path = MOE_PATH_AUTO;
+    moe::BlobLayout L{};
+    int S = 0;                     // slots per token (top_k + n_shared)
+    std::vector<void *> allocs;
+    // token quantisation
+    int8_t *xq = nullptr;
+    float *sa = nullptr;
+    // router
+    double *logits = nullptr;
+    int32_t *idx = nullptr;
+    float *gw = nullptr;
+    // routing lists
+    int32_t *cnt = nullptr, *list = nullptr, *active = nullptr, *n_active = nullptr;
+    uint32_t *done = nullptr;
+    // expert FFN intermediates, one row per slot
+    float *h = nullptr;
+    int8_t *qh = nullptr;
+    float *sh = nullptr;
+    float *Y = nullptr;
+    // MFMA path: tile work list
+    int32_t *tiles = nullptr, *n_tiles = nullptr;
+    int max_tiles = 0;
+    // MXFP4 path: bf16 activations of h
+    uint16_t *hb = nullptr;
+    // small device constants for single-blob projections
+    int32_t *zero1 = nullptr, *one1 = nullptr, *dbg_cnt = nullptr, *ident = nullptr;
+    int last_T = 0;
+    // kernel timing
+    bool prof_on = false;
+    hipEvent_t prof_ev[2 * MOE_PROF_N] = {};
+    bool prof_used[MOE_PROF_N] = {};
+    double prof_ms[MOE_PROF_N] = {};
+    int64_t prof_cnt[MOE_PROF_N] = {};
+};
+
+namespace moe {
+
+moe_status fail(moe_status st, const char *fmt, ...);
+moe_status hip_fail(hipError_t e, const char *what);
+moe_status validate_desc(const moe_layer_desc *d);
+moe_status check_device(int device);
+
+// Kernel timing helpers: prof_begin/prof_end bracket one launch of kind `k`;
+// prof_collect waits for the call's events and accumulates.
+void prof_begin(moe_ctx *c, int k, hipStream_t st);
+void prof_end(moe_ctx *c, int k, hipStream_t st);
+moe_status prof_collect(moe_ctx *c);
+
+// kernel path selection
+bool use_mfma(const moe_ctx *c, int T);
+
+// MFMA grouped GEMM path (kernels_gemm.hip)
+hipError_t launch_mfma_tiles(moe_ctx *c, int T, hipStream_t st);
+hipError_t launch_mfma_tiles_single(moe_ctx *c, int T, hipStream_t st);
+hipError_t launch_gateup_mfma(const ProjArgs &a, const moe_ctx *c, int T, int F, float *h, int ldh,
+                              hipStream_t st);
+hipError_t launch_proj_mfma(const ProjArgs &a, const moe_ctx *c, int T, int n_rows,
+                            hipStream_t st);
+size_t mfma_max_tiles(int T, int E, int n_shared);
+
+// MXFP4 path (kernels_mx.hip)
+moe_status mx_ffn_enqueue(moe_ctx *c, const void *x, int T, const moe_layer_weights *w,
+                          const void *const *expert_ptrs, const int32_t *idx, const float *gw,
+                          void *out, hipStream_t st);
+
+// small helpers (kernels_router.hip)
+hipError_t launch_set_i32(int32_t *p, int32_t v, hipStream_t st);
+
+// cache (cache.cpp): DEMAND stage of the routed experts of `layer` for the
+// T*k device ids in idx; returns the device pointer table for the layer.
+moe_status cache_demand_for_layer(moe_cache *cache, const moe_layer_desc &d, int layer,
+                                  const int32_t *idx_dev, int T, hipStream_t compute,
+                                  const void *const **table);
+
+}  // namespace moe

@@ -1,0 +1,383 @@
+// kernels_router.hip -- activation quantisation, sigmoid router, top-k and the
+// token->expert permutation for gfx950.
+//
+// Router: DeepSeek-V3 style ("Guide Complet de Colibri", table "Points
+// techniques cles", router row): sigmoid scores, a bias that only steers the
+// selection, the k best experts per token, weights normalised over the
+// selected experts and multiplied by the routed scale.  Logits and scores are
+// computed in fp64 so that the choice does not depend on summation order.
+#include "device_common.h"
+#include "moe_internal.h"
+
+#include <climits>
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Per-token int8 quantisation: amax over the row, inv = 127/amax and
+// s = amax/127 in fp32 (correctly rounded), q = clamp(rint(x*inv), -127, 127).
+// One 256-thread block per token.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_tokens_kernel(const uint16_t *__restrict__ x, int H,
+                                                           int8_t *__restrict__ q,
+                                                           float *__restrict__ s)
+{
+    __shared__ float red[4];
+    const int t = blockIdx.x;
+    const uint16_t *xr = x + (size_t)t * H;
+    float amax = 0.0f;
+    for (int i = threadIdx.x * 8; i < H; i += 2048) {
+        uint4 v = *reinterpret_cast<const uint4 *>(xr + i);
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            amax = fmaxf(amax, fabsf(bf16_to_f32(w[j] & 0xffffu)));
+            amax = fmaxf(amax, fabsf(bf16_to_f32(w[j] >> 16)));
+        }
+    }
+    amax = block_max_256(amax, red);
+    float inv = 0.0f, sc = 0.0f;
+    if (amax > 0.0f) {
+        inv = 127.0f / amax;
+        sc = amax / 127.0f;
+    }
+    int8_t *qr = q + (size_t)t * H;
+    for (int i = threadIdx.x * 8; i < H; i += 2048) {
+        uint4 v = *reinterpret_cast<const uint4 *>(xr + i);
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float xv = bf16_to_f32((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu));
+            float r = rintf(xv * inv);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            int qi = (int)r;
+            packed[j >> 2] |= ((uint32_t)qi & 0xffu) << (8 * (j & 3));
+        }
+        *reinterpret_cast<uint2 *>(qr + i) = make_uint2(packed[0], packed[1]);
+    }
+    if (threadIdx.x == 0)
+        s[t] = sc;
+}
+
+hipError_t launch_quant_tokens(const uint16_t *x, int T, int H, int8_t *q, float *s,
+                               hipStream_t st)
+{
+    if (T <= 0)
+        return hipSuccess;
+    quant_tokens_kernel<<<T, 256, 0, st>>>(x, H, q, s);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Router logits l[t,e] = sum_k x[t,k]*Wr[e,k] in fp64 (bf16 x fp32 products
+// are exact in fp64).
+// Few tokens: one wave per expert streams its router row with 16-byte loads
+// for up to TB tokens.  Many tokens: 64x64 output tiles through LDS.
+// ---------------------------------------------------------------------------
+template <int TB>
+__global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t *__restrict__ x, int T,
+                                                          int H, const float *__restrict__ Wr,
+                                                          int E, double *__restrict__ logits)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int e = blockIdx.x * 4 + wave;
+    if (e >= E)
+        return;
+    const int t0 = blockIdx.y * TB;
+    const float *w = Wr + (size_t)e * H;
+    double acc[TB];
+#pragma unroll
+    for (int m = 0; m < TB; ++m)
+        acc[m] = 0.0;
+    for (int k = lane * 4; k < H; k += 256) {
+        float4 wv = *reinterpret_cast<const float4 *>(w + k);
+#pragma unroll
+        for (int m = 0; m < TB; ++m) {
+            if (t0 + m < T) {
+                uint2 xv = *reinterpret_cast<const uint2 *>(x + (size_t)(t0 + m) * H + k);
+                acc[m] = fma((double)bf16_to_f32(xv.x & 0xffffu), (double)wv.x, acc[m]);
+                acc[m] = fma((double)bf16_to_f32(xv.x >> 16), (double)wv.y, acc[m]);
+                acc[m] = fma((double)bf16_to_f32(xv.y & 0xffffu), (double)wv.z, acc[m]);
+                acc[m] = fma((double)bf16_to_f32(xv.y >> 16), (double)wv.w, acc[m]);
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < TB; ++m) {
+        double v = wave_sum_d(acc[m]);
+        if (lane == 0 && t0 + m < T)
+            logits[(size_t)(t0 + m) * E + e] = v;
+    }
+}
+
+// 64 tokens x 64 experts per block, each thread a 4x4 register tile; K in
+// steps of 32 through LDS (values widened to fp64 once, on the way in).
+__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__restrict__ x, int T,
+                                                          int H, const float *__restrict__ Wr,
+                                                          int E, double *__restrict__ logits)
+{
+    constexpr int TM = 64, TN = 64, KS = 32;
+    __shared__ double xs[KS][TM + 1];
+    __shared__ double ws[KS][TN + 1];
+    const int tm0 = blockIdx.y * TM, tn0 = blockIdx.x * TN;
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;   // 16 x 16 threads
+    double acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = 0.0;
+    for (int k0 = 0; k0 < H; k0 += KS) {
+        // load 64 x 32 of x and of Wr: 2048 values each, 8 per thread
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            int v = threadIdx.x + it * 256;
+            int row = v >> 5, kk = v & 31;
+            int t = tm0 + row, e = tn0 + row;
+            xs[kk][row] = (t < T) ? (double)bf16_to_f32(x[(size_t)t * H + k0 + kk]) : 0.0;
+            ws[kk][row] = (e < E) ? (double)Wr[(size_t)e * H + k0 + kk] : 0.0;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int kk = 0; kk < KS; ++kk) {
+            double a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                a[i] = xs[kk][ty + 16 * i];
+                b[i] = ws[kk][tx + 16 * i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = fma(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int t = tm0 + ty + 16 * i, e = tn0 + tx + 16 * j;
+            if (t < T && e < E)
+                logits[(size_t)t * E + e] = acc[i][j];
+        }
+}
+
+hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *Wr, int E,
+                                double *logits, hipStream_t st)
+{
+    if (T <= 0)
+        return hipSuccess;
+    if (T <= 16) {
+        dim3 grid((E + 3) / 4, (T + 3) / 4);
+        router_gemv_kernel<4><<<grid, 256, 0, st>>>(x, T, H, Wr, E, logits);
+    } else {
+        dim3 grid((E + 63) / 64, (T + 63) / 64);
+        router_gemm_kernel<<<grid, 256, 0, st>>>(x, T, H, Wr, E, logits);
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Top-k per token, one wave per token.  Score s = 1/(1+exp(-l)), choice
+// c = s + bias (fp64).  k rounds of a wave-wide argmax over (c desc, index
+// asc); NaN choices rank as -inf.  Gate weights s/sum(s)*r summed in rank
+// order.  E <= 1024 (16 candidates per lane).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ logits,
+                                                   const float *__restrict__ bias, int T, int E,
+                                                   int k, float r, int32_t *__restrict__ idx,
+                                                   float *__restrict__ w)
+{
+    constexpr int PL = 16;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T)
+        return;
+    double c[PL], s[PL];
+#pragma unroll
+    for (int j = 0; j < PL; ++j) {
+        int e = lane + 64 * j;
+        if (e < E) {
+            double l = logits[(size_t)t * E + e];
+            s[j] = 1.0 / (1.0 + exp(-l));
+            double cv = s[j] + (double)bias[e];
+            c[j] = (cv != cv) ? -INFINITY : cv;
+        } else {
+            s[j] = 0.0;
+            c[j] = -INFINITY;
+        }
+    }
+    uint32_t taken = 0u;
+    int sel_e[16];
+    double sel_s[16];
+    for (int i = 0; i < k; ++i) {
+        double bc = -INFINITY, bs = 0.0;
+        int be = INT_MAX;
+#pragma unroll
+        for (int j = 0; j < PL; ++j) {
+            int e = lane + 64 * j;
+            if (e < E && !((taken >> j) & 1u)) {
+                if (c[j] > bc || (c[j] == bc && e < be)) {
+                    bc = c[j];
+                    be = e;
+                    bs = s[j];
+                }
+            }
+        }
+        for (int m = 32; m >= 1; m >>= 1) {
+            double oc = __shfl_xor(bc, m, 64);
+            int oe = __shfl_xor(be, m, 64);
+            double os = __shfl_xor(bs, m, 64);
+            if (oc > bc || (oc == bc && oe < be)) {
+                bc = oc;
+                be = oe;
+                bs = os;
+            }
+        }
+        if ((be & 63) == lane)
+            taken |= 1u << (be >> 6);
+        sel_e[i] = be;
+        sel_s[i] = bs;
+    }
+    if (lane == 0) {
+        double den = 0.0;
+        for (int i = 0; i < k; ++i)
+            den += sel_s[i];
+        for (int i = 0; i < k; ++i) {
+            double wi = (den > 0.0) ? (sel_s[i] / den) * (double)r : 0.0;
+            idx[(size_t)t * k + i] = sel_e[i];
+            w[(size_t)t * k + i] = (float)wi;
+        }
+    }
+}
+
+hipError_t launch_topk(const double *logits, const float *bias, int T, int E, int k, float r,
+                       int32_t *idx, float *w, hipStream_t st)
+{
+    if (T <= 0)
+        return hipSuccess;
+    topk_kernel<<<(T + 3) / 4, 256, 0, st>>>(logits, bias, T, E, k, r, idx, w);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Token -> expert permutation.  Block e (e < E) collects, in token order, the
+// slots t*S+i with idx[t,i] == e (ordered compaction by wave ballots); block E
+// (shared expert, when present) takes every token at slot t*S+k.  The last
+// block to finish lists the experts that received rows, in expert order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void permute_kernel(const int32_t *__restrict__ idx, int T,
+                                                      int k, int E, int n_shared,
+                                                      int32_t *__restrict__ cnt,
+                                                      int32_t *__restrict__ list,
+                                                      int list_stride,
+                                                      int32_t *__restrict__ active,
+                                                      int32_t *__restrict__ n_active,
+                                                      uint32_t *__restrict__ done)
+{
+    __shared__ int wcnt[4];
+    __shared__ int last;
+    const int e = blockIdx.x;
+    const int S = k + n_shared;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    int total = 0;
+    int32_t *mine = list + (size_t)e * list_stride;
+    if (e < E) {
+        const int N = T * k;
+        for (int j0 = 0; j0 < N; j0 += 256) {
+            int j = j0 + threadIdx.x;
+            bool m = (j < N) && (idx[j] == e);
+            uint64_t bal = __ballot(m);
+            int pre = __popcll(bal & ((1ull << lane) - 1ull));
+            if (lane == 0)
+                wcnt[wave] = __popcll(bal);
+            __syncthreads();
+            int off = total;
+            for (int v = 0; v < wave; ++v)
+                off += wcnt[v];
+            // ids repeated within a token (not allowed by the API) could give
+            // an expert more rows than its list holds: extra rows are dropped
+            if (m && off + pre < list_stride) {
+                int t = j / k, i = j - (j / k) * k;
+                mine[off + pre] = t * S + i;
+            }
+            total += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+            __syncthreads();
+        }
+    } else {
+        for (int t = threadIdx.x; t < T; t += 256)
+            mine[t] = t * S + k;
+        total = T;
+    }
+    if (threadIdx.x == 0) {
+        cnt[e] = total < list_stride ? total : list_stride;
+        __threadfence();
+        unsigned prev = atomicAdd(done, 1u);
+        last = (prev == gridDim.x - 1) ? 1 : 0;
+    }
+    __syncthreads();
+    if (!last || wave != 0)
+        return;
+    __threadfence();
+    const int nE = gridDim.x;
+    int na = 0;
+    for (int e0 = 0; e0 < nE; e0 += 64) {
+        int ee = e0 + lane;
+        int c = (ee < nE) ? __atomic_load_n(&cnt[ee], __ATOMIC_RELAXED) : 0;
+        uint64_t bal = __ballot(c > 0);
+        if (c > 0)
+            active[na + __popcll(bal & ((1ull << lane) - 1ull))] = ee;
+        na += __popcll(bal);
+    }
+    if (lane == 0) {
+        *n_active = na;
+        *done = 0u;
+    }
+}
+
+hipError_t launch_permute(const int32_t *idx, int T, int k, int E, int n_shared, int32_t *cnt,
+                          int32_t *list, int list_stride, int32_t *active, int32_t *n_active,
+                          uint32_t *done_counter, hipStream_t st)
+{
+    permute_kernel<<<E + n_shared, 256, 0, st>>>(idx, T, k, E, n_shared, cnt, list, list_stride,
+                                                  active, n_active, done_counter);
+    return hipGetLastError();
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Small helpers.
+// ---------------------------------------------------------------------------
+__global__ void set_i32_kernel(int32_t *p, int32_t v)
+{
+    *p = v;
+}
+
+hipError_t launch_set_i32(int32_t *p, int32_t v, hipStream_t st)
+{
+    set_i32_kernel<<<1, 1, 0, st>>>(p, v);
+    return hipGetLastError();
+}
+
+__global__ void table_update_kernel(const void **table, int set_idx, const void *ptr,
+                                    int clear_idx)
+{
+    if (clear_idx >= 0)
+        table[clear_idx] = nullptr;
+    table[set_idx] = ptr;
+}
+
+hipError_t launch_table_update(const void **table, int set_idx, const void *ptr, int clear_idx,
+                               hipStream_t st)
+{
+    table_update_kernel<<<1, 1, 0, st>>>(table, set_idx, ptr, clear_idx);
+    return hipGetLastError();
+}
+
+}  // namespace moe

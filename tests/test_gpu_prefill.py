@@ -1,0 +1,120 @@
+"""GPU parity of the grouped int4 x int8 GEMM on the int8 MFMA (prefill path)
+through the C ABI: exact integer accumulators, bit-equality with the oracle
+and with the GEMV path, and a skewed-routing prefill layer at full width."""
+import numpy as np
+import pytest
+
+import oracle
+from quantized_expert_ffn_topk_amd import abi, synth
+from tests.gpu_common import Case, check_out, check_routing
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+def _unit_case(seed, H, F, g):
+    ex = synth.expert_int4(seed, 0, H, F, g)
+    for k in ("s_gate", "s_up", "s_down"):
+        ex[k] = np.full_like(ex[k], 0x3C00)
+    c = Case(seed, 1, H, F, 4, 2, 0, g)
+    c.distinct = [ex]
+    c.emap = [0] * 4
+    return c, ex
+
+
+@pytest.mark.parametrize("T", [1, 37, 64, 130])
+@pytest.mark.parametrize("part", [0, 1, 2])
+def test_mfma_project_unit_scales_equal_integer_dots(T, part):
+    H, F, g = 512, 256, 32
+    c, ex = _unit_case(11, H, F, g)
+    lay = c.layer(max_tokens=256, path=abi.PATH_MFMA)
+    K = F if part == 2 else H
+    N = H if part == 2 else F
+    r = np.random.default_rng(T + 100 * part)
+    q = r.integers(-127, 128, size=(T, K)).astype(np.int8)
+    y = torch.empty((T, N), dtype=torch.float32, device="cuda")
+    abi.moe_debug_project(lay.ctx, lay.blobs[0], part, torch.from_numpy(q).cuda(),
+                          torch.ones(T, dtype=torch.float32, device="cuda"), T, y)
+    _sync()
+    W = ex[("q_gate", "q_up", "q_down")[part]].astype(np.int64)
+    assert np.array_equal(y.cpu().numpy().astype(np.int64), q.astype(np.int64) @ W.T)
+    lay.close()
+
+
+@pytest.mark.parametrize("g", [32, 64])
+def test_mfma_project_bit_exact_vs_oracle_and_gemv(g):
+    H, F, T = 768, 512, 70
+    c = Case(12, 1, H, F, 4, 2, 0, g)
+    ex = c.distinct[0]
+    lay = c.layer(max_tokens=128)
+    r = np.random.default_rng(g)
+    for part in range(3):
+        K = F if part == 2 else H
+        N = H if part == 2 else F
+        q = r.integers(-127, 128, size=(T, K)).astype(np.int8)
+        s = r.uniform(1e-3, 1e-1, size=T).astype(np.float32)
+        qd, sd = torch.from_numpy(q).cuda(), torch.from_numpy(s).cuda()
+        outs = []
+        for path in (abi.PATH_MFMA, abi.PATH_GEMV):
+            lay.set_path(path)
+            y = torch.empty((T, N), dtype=torch.float32, device="cuda")
+            abi.moe_debug_project(lay.ctx, lay.blobs[0], part, qd, sd, T, y)
+            _sync()
+            outs.append(y.cpu().numpy())
+        assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32)), part
+        W = ex[("q_gate", "q_up", "q_down")[part]]
+        S = ex[("s_gate", "s_up", "s_down")[part]]
+        for t in (0, 33, T - 1):
+            ref = oracle.proj_i4i8(q[t], s[t], W, S, g)
+            assert np.array_equal(outs[0][t].view(np.uint32), ref.view(np.uint32)), (part, t)
+    lay.close()
+
+
+@pytest.mark.parametrize("T,g", [(100, 32), (257, 64)])
+def test_mfma_layer_equals_gemv_layer_and_oracle(T, g):
+    c = Case(13, T, 512, 256, 16, 4, 1, g=g, r=2.5)
+    lay = c.layer(max_tokens=T)
+    xd = lay.x_tensor(c.x)
+    res = {}
+    for path in (abi.PATH_MFMA, abi.PATH_GEMV):
+        lay.set_path(path)
+        idx, w, out = lay.forward(xd)
+        _sync()
+        res[path] = (idx.cpu().numpy(), w.cpu().numpy(), out.cpu().numpy())
+    assert np.array_equal(res[abi.PATH_MFMA][2].view(np.uint32), res[abi.PATH_GEMV][2].view(np.uint32))
+    idx_o, w_o, out_o = c.oracle_layer()
+    _, _, _, _, ch_o = c.oracle_router()
+    check_routing(res[abi.PATH_MFMA][0], res[abi.PATH_MFMA][1], idx_o, w_o, ch_o)
+    check_out(res[abi.PATH_MFMA][2], out_o)
+    lay.close()
+
+
+def test_glm_prefill_zipf_full_size_sampled():
+    # GLM-shaped prefill: 4096 tokens, hidden 6144, 256 routed + 1 shared,
+    # F 2048, top-8, routed scale 2.5, Zipf(1.1)-skewed selection bias.
+    # Routing is checked for every token; outputs of 6 sampled tokens on 128
+    # sampled columns against the oracle.
+    H, F, E, k, T = 6144, 2048, 256, 8, 4096
+    c = Case(0, T, H, F, E, k, 1, r=2.5, n_distinct=3, bias=synth.zipf_bias(0, E))
+    lay = c.layer(max_tokens=T)
+    idx, w, out = lay.forward(lay.x_tensor(c.x))
+    _sync()
+    ig, wg, og = idx.cpu().numpy(), w.cpu().numpy(), out.cpu().numpy()
+    idx_o, w_o, lg, sc, ch = oracle.router(c.x, c.Wr, c.b, k, c.r, want=True)
+    check_routing(ig, wg, idx_o, w_o, ch)
+    loads = np.bincount(ig.ravel(), minlength=E)
+    print("expert loads: max %d, empty %d, top-8 share %.3f" % (
+        loads.max(), int((loads == 0).sum()), np.sort(loads)[::-1][:8].sum() / loads.sum()))
+    rng = np.random.default_rng(1)
+    toks = np.sort(rng.choice(T, 6, replace=False))
+    cols = np.sort(rng.choice(H, 128, replace=False)).astype(np.int32)
+    sub = Case(0, 6, H, F, E, k, 1, r=2.5, n_distinct=3, bias=c.b, x=c.x[toks])
+    sub.distinct, sub.shared, sub.Wr = c.distinct, c.shared, c.Wr
+    _, _, out_o = sub.oracle_layer(out_rows=cols)
+    check_out(og[toks][:, cols], out_o)
+    lay.close()
