@@ -16,7 +16,7 @@
 // row 8*(r/4) + 4*(l/32) + r%4, weight row l%32.  Each lane therefore needs a
 // single scale per chunk.
 //
-// Work list: tiles of up to 64 rows of one expert (built on the device from
+// Work list: tiles of up to 128 rows of one expert (built on the device from
 // the per-expert counts, no host synchronisation).  Blocks are remapped so
 // that each XCD walks a contiguous run of tiles of the same expert and weight
 // block, keeping that block in its own L2.
@@ -28,7 +28,7 @@ namespace moe {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int MT = 64;     // activation rows per tile
+constexpr int MT = 128;    // activation rows per tile
 
 bool use_mfma(const moe_ctx *c, int T)
 {
@@ -55,7 +55,7 @@ static int tiles_bound(const moe_ctx *c, int T)
 }
 
 // ---------------------------------------------------------------------------
-// Tile list: for experts 0..n_exp-1 in order, ceil(cnt/64) tiles (e, m0).
+// Tile list: for experts 0..n_exp-1 in order, ceil(cnt/128) tiles (e, m0).
 // One block of 1024 threads; n_exp <= 2048.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void mfma_tiles_kernel(const int32_t *__restrict__ cnt,
@@ -103,10 +103,6 @@ hipError_t launch_mfma_tiles_single(moe_ctx *c, int T, hipStream_t st)
 // ---------------------------------------------------------------------------
 // Shared pieces.
 // ---------------------------------------------------------------------------
-struct TileRows {
-    int e, m0, mc;
-};
-
 // Block index -> (weight block nb, tile mt): each XCD (blocks b with the same
 // b % 8) gets a contiguous run of logical indices, tile index fastest.  The
 // grid is padded to a multiple of 8; padding blocks get nb >= n_blocks.
@@ -117,26 +113,6 @@ __device__ __forceinline__ void block_coords(int mt_max, int *nb, int *mt)
     const int logical = (b & 7) * (nwg >> 3) + (b >> 3);
     *nb = logical / mt_max;
     *mt = logical - *nb * mt_max;
-}
-
-// Stages the tile's slots and row scales; -1 marks rows past the expert's end.
-__device__ __forceinline__ void stage_tile(const ProjArgs &a, int e, int m0, int mc, int *s_slot,
-                                           int *s_row, float *s_sc)
-{
-    if (threadIdx.x < MT) {
-        const int i = threadIdx.x;
-        int slot = -1, row = -1;
-        float sc = 0.0f;
-        if (i < mc) {
-            slot = a.rt.list[(size_t)e * a.rt.list_stride + m0 + i];
-            row = a.in_by_token ? slot / a.rt.S : slot;
-            sc = a.s[row];
-        }
-        s_slot[i] = slot;
-        s_row[i] = row;
-        s_sc[i] = sc;
-    }
-    __syncthreads();
 }
 
 __device__ __forceinline__ v4i nibble_bytes(uint4 w, int shift)
@@ -160,107 +136,90 @@ __device__ __forceinline__ v4i as_v4i(uint4 w)
 }
 
 // ---------------------------------------------------------------------------
-// Gate/up + SwiGLU.  Block = 64 rows x 64 outputs n (64 gate + 64 up weight
-// rows); wave (wm, wn) = rows [32wm, +32) x n [32wn, +32), two MFMAs per chunk.
-// GS = chunks per scale group (1 for group 32, 2 for group 64).
+// One kernel body for both projections.  A block owns a tile of up to 128
+// activation rows of one expert and 128 weight rows:
+//   GATEUP: gate rows n and up rows n for n in [64nb, 64nb+64), output
+//           h = fp32(silu(G)*U) (G, U scaled by the token scale);
+//   PROJ  : weight rows [128nb, 128nb+128) (down projection, or one part of
+//           the gate/up section), output fp32(sum * row scale).
+// K is walked in stages of 4 chunks (128 inputs).  Each stage's activation
+// rows (128 x 128 B) and weight nibbles (128 x 64 B) are staged in LDS, double
+// buffered, rows padded so that 16-byte LDS reads are free of bank conflicts.
+// Wave w: weight-row blocks rb0, rb1 (32 rows each) and activation-row blocks
+// 2*(w>>1), 2*(w>>1)+1: four MFMAs per chunk; empty activation blocks of a
+// partly filled tile are skipped.
 // ---------------------------------------------------------------------------
+constexpr int KB = 4;                      // chunks per stage
+constexpr int A_LD = KB * 32 + 16;         // LDS row pitch of activations (bytes)
+constexpr int B_LD = KB * 16 + 16;         // LDS row pitch of weight nibbles
+constexpr int A_STAGE = MT * A_LD;
+constexpr int B_STAGE = 128 * B_LD;
+
+// One stage (KB chunks) of one wave: its activation block (32 rows) against
+// the lane's two weight rows.  Per scale group: MFMA into a fresh int32 tile,
+// then the exact fp64 epilogue acc += (int32 result) * scale/16.
 template <int GS>
-__global__ __launch_bounds__(256) void gateup_mfma_kernel(ProjArgs a, const int2 *__restrict__ tiles,
-                                                          const int32_t *__restrict__ n_tiles,
-                                                          int mt_max, int n_blocks,
-                                                          float *__restrict__ h, int ldh)
+__device__ __forceinline__ void stage_compute(const uint8_t *__restrict__ A,
+                                              const uint8_t *__restrict__ B, int arow, int R0,
+                                              int R1, int hh, int shift, const uint16_t *sv0,
+                                              const uint16_t *sv1, double (&acc)[2][16])
 {
-    __shared__ int s_slot[MT], s_row[MT];
-    __shared__ float s_sc[MT];
-    int nb, mt;
-    block_coords(mt_max, &nb, &mt);
-    if (nb >= n_blocks || mt >= *n_tiles)
-        return;
-    const int2 tl = tiles[mt];
-    const int e = tl.x, m0 = tl.y;
-    const int mc = min(MT, a.rt.cnt[e] - m0);
-    stage_tile(a, e, m0, mc, s_slot, s_row, s_sc);
-
-    const uint8_t *blob =
-        reinterpret_cast<const uint8_t *>((e == a.ex.E) ? a.ex.shared : a.ex.ptrs[e]);
-    const int K = a.K, KC = K >> 5;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wm = wave & 1, wn = wave >> 1;
-    const int hh = lane >> 5, li = lane & 31;
-    const int arow = s_row[32 * wm + li];
-    const uint8_t *ap = reinterpret_cast<const uint8_t *>(a.q) + (size_t)(arow < 0 ? 0 : arow) * K + 16 * hh;
-    const int n = 64 * nb + 32 * wn + li;
-    const int bt = 2 * (n >> 4), br = n & 15;
-    const uint8_t *bg = blob + a.w_off + (size_t)bt * a.tile_w + br * 16;
-    const uint8_t *bu = bg + a.tile_w;
-    const uint16_t *sg = reinterpret_cast<const uint16_t *>(blob + a.s_off + (size_t)bt * a.tile_s) + br;
-    const uint16_t *su = reinterpret_cast<const uint16_t *>(blob + a.s_off + (size_t)(bt + 1) * a.tile_s) + br;
-    const int shift = hh ? 0 : 4;
-
-    double pg[16], pu[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        pg[r] = 0.0;
-        pu[r] = 0.0;
-    }
-    constexpr int U = 4;
-    for (int c0 = 0; c0 < KC; c0 += U) {
-        uint4 av[U], gv[U], uv[U];
-        uint16_t sgv[U / GS], suv[U / GS];
+    for (int u = 0; u < KB; u += GS) {
+        const double s0 = (double)f16_to_f32(sv0[u / GS]) * 0.0625;
+        const double s1 = (double)f16_to_f32(sv1[u / GS]) * 0.0625;
+        v4i a[GS];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            av[u] = *reinterpret_cast<const uint4 *>(ap + (size_t)(c0 + u) * 32);
-            gv[u] = *reinterpret_cast<const uint4 *>(bg + (size_t)(c0 + u) * 256);
-            uv[u] = *reinterpret_cast<const uint4 *>(bu + (size_t)(c0 + u) * 256);
-        }
+        for (int v = 0; v < GS; ++v)
+            a[v] = as_v4i(*reinterpret_cast<const uint4 *>(A + arow * A_LD + (u + v) * 32 + 16 * hh));
+        const v16i zero = {0};
+        v16i d = zero;
 #pragma unroll
-        for (int u = 0; u < U / GS; ++u) {
-            sgv[u] = sg[(size_t)(c0 / GS + u) * 16];
-            suv[u] = su[(size_t)(c0 / GS + u) * 16];
-        }
+        for (int v = 0; v < GS; ++v)
+            d = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                a[v], nibble_bytes(*reinterpret_cast<const uint4 *>(B + R0 * B_LD + (u + v) * 16), shift),
+                d, 0, 0, 0);
 #pragma unroll
-        for (int u = 0; u < U; u += GS) {
-            v16i dg = {0}, du = {0};
+        for (int r = 0; r < 16; ++r)
+            acc[0][r] = fma((double)d[r], s0, acc[0][r]);
+        d = zero;
 #pragma unroll
-            for (int v = 0; v < GS; ++v) {
-                v4i A = as_v4i(av[u + v]);
-                dg = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, nibble_bytes(gv[u + v], shift), dg, 0, 0, 0);
-                du = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, nibble_bytes(uv[u + v], shift), du, 0, 0, 0);
-            }
-            const double sgd = (double)f16_to_f32(sgv[u / GS]) * 0.0625;
-            const double sud = (double)f16_to_f32(suv[u / GS]) * 0.0625;
+        for (int v = 0; v < GS; ++v)
+            d = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                a[v], nibble_bytes(*reinterpret_cast<const uint4 *>(B + R1 * B_LD + (u + v) * 16), shift),
+                d, 0, 0, 0);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                pg[r] = fma((double)dg[r], sgd, pg[r]);
-                pu[r] = fma((double)du[r], sud, pu[r]);
-            }
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int tok = 32 * wm + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const int slot = s_slot[tok];
-        if (slot >= 0) {
-            const double sa = (double)s_sc[tok];
-            const double G = pg[r] * sa, Uv = pu[r] * sa;
-            h[(size_t)slot * ldh + n] = (float)(G / (1.0 + exp(-G)) * Uv);
-        }
+        for (int r = 0; r < 16; ++r)
+            acc[1][r] = fma((double)d[r], s1, acc[1][r]);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Plain projection (down, or one part of gate/up for inspection).  Block =
-// 64 rows x 128 outputs; wave (wm, wn) = rows [32wm, +32) x outputs
-// [64wn, +64) as two 32-wide MFMA columns.  Output row n lives in tile
-// tile_base + (n/32)*pair_stride + ((n/16)%2)*j_stride, row n%16.
+// One kernel body for both projections.  A block (8 waves) owns a tile of up
+// to 128 activation rows of one expert and 128 weight rows:
+//   GATEUP: gate rows n and up rows n for n in [64nb, 64nb+64), output
+//           h = fp32(silu(G)*U) (G, U scaled by the token scale);
+//   PROJ  : weight rows [128nb, 128nb+128) (down projection, or one part of
+//           the gate/up section), output fp32(sum * row scale).
+// K is walked in stages of 4 chunks (128 inputs).  Each stage's activation
+// rows (128 x 128 B) and weight nibbles (128 x 64 B) are staged in LDS, double
+// buffered, rows padded so that 16-byte LDS reads are free of bank conflicts.
+// Wave w: activation block w&3 (32 rows) and weight blocks rb0, rb1 (32 rows
+// each): two MFMAs per chunk.  Waves whose block is past the expert's rows
+// only help staging.
 // ---------------------------------------------------------------------------
-template <int GS>
-__global__ __launch_bounds__(256) void proj_mfma_kernel(ProjArgs a, const int2 *__restrict__ tiles,
-                                                        const int32_t *__restrict__ n_tiles,
-                                                        int mt_max, int n_blocks)
+template <bool GATEUP, int GS>
+__global__ __launch_bounds__(512, 1) void mfma_proj_kernel(ProjArgs a, const int2 *__restrict__ tiles,
+                                                           const int32_t *__restrict__ n_tiles,
+                                                           int mt_max, int n_blocks,
+                                                           float *__restrict__ out, int ldo)
 {
+    __shared__ __align__(16) uint8_t lds_a[2 * A_STAGE];
+    __shared__ __align__(16) uint8_t lds_b[2 * B_STAGE];
     __shared__ int s_slot[MT], s_row[MT];
     __shared__ float s_sc[MT];
+    __shared__ int s_tile[8];
+
     int nb, mt;
     block_coords(mt_max, &nb, &mt);
     if (nb >= n_blocks || mt >= *n_tiles)
@@ -268,73 +227,131 @@ __global__ __launch_bounds__(256) void proj_mfma_kernel(ProjArgs a, const int2 *
     const int2 tl = tiles[mt];
     const int e = tl.x, m0 = tl.y;
     const int mc = min(MT, a.rt.cnt[e] - m0);
-    stage_tile(a, e, m0, mc, s_slot, s_row, s_sc);
+    const int tid = threadIdx.x;
+    if (tid < MT) {
+        int slot = -1, row = -1;
+        float sc = 0.0f;
+        if (tid < mc) {
+            slot = a.rt.list[(size_t)e * a.rt.list_stride + m0 + tid];
+            row = a.in_by_token ? slot / a.rt.S : slot;
+            sc = a.s[row];
+        }
+        s_slot[tid] = slot;
+        s_row[tid] = row;
+        s_sc[tid] = sc;
+    }
+    if (tid < 8) {
+        // blob tile of LDS weight rows [16*tid, 16*tid+16)
+        int t;
+        if (GATEUP) {
+            t = (tid < 4) ? 2 * (4 * nb + tid) : 2 * (4 * nb + tid - 4) + 1;
+        } else {
+            const int n = 128 * nb + 16 * tid;
+            t = a.tile_base + (n >> 5) * a.pair_stride + ((n >> 4) & 1) * a.j_stride;
+        }
+        s_tile[tid] = t;
+    }
+    __syncthreads();
 
     const uint8_t *blob =
         reinterpret_cast<const uint8_t *>((e == a.ex.E) ? a.ex.shared : a.ex.ptrs[e]);
-    const int K = a.K, KC = K >> 5;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wm = wave & 1, wn = wave >> 1;
-    const int hh = lane >> 5, li = lane & 31;
-    const int arow = s_row[32 * wm + li];
-    const uint8_t *ap = reinterpret_cast<const uint8_t *>(a.q) + (size_t)(arow < 0 ? 0 : arow) * K + 16 * hh;
-    const int n0 = 128 * nb + 64 * wn + li, n1 = n0 + 32;
-    const int t0 = a.tile_base + (n0 >> 5) * a.pair_stride + ((n0 >> 4) & 1) * a.j_stride;
-    const int t1 = a.tile_base + (n1 >> 5) * a.pair_stride + ((n1 >> 4) & 1) * a.j_stride;
-    const uint8_t *b0 = blob + a.w_off + (size_t)t0 * a.tile_w + (n0 & 15) * 16;
-    const uint8_t *b1 = blob + a.w_off + (size_t)t1 * a.tile_w + (n1 & 15) * 16;
-    const uint16_t *s0 = reinterpret_cast<const uint16_t *>(blob + a.s_off + (size_t)t0 * a.tile_s) + (n0 & 15);
-    const uint16_t *s1 = reinterpret_cast<const uint16_t *>(blob + a.s_off + (size_t)t1 * a.tile_s) + (n1 & 15);
-    const int shift = hh ? 0 : 4;
+    const int K = a.K, KC = K >> 5, n_stages = KC / KB;
+    const uint8_t *qbase = reinterpret_cast<const uint8_t *>(a.q);
 
-    double p0[16], p1[16];
+    // global -> LDS assignment: activations 1024 pieces of 16 B (2/thread),
+    // weights 512 pieces (1/thread)
+    const uint8_t *ga[2];
+    int la[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int p = tid + 512 * j;
+        const int tok = p >> 3, seg = p & 7;
+        const int row = s_row[tok];
+        ga[j] = qbase + (size_t)(row < 0 ? s_row[0] : row) * K + seg * 16;
+        la[j] = tok * A_LD + seg * 16;
+    }
+    const uint8_t *gb;
+    int lb;
+    {
+        const int r = tid & 15, kcl = (tid >> 4) & 3, tj = tid >> 6;
+        gb = blob + a.w_off + (size_t)s_tile[tj] * a.tile_w + kcl * 256 + r * 16;
+        lb = (16 * tj + r) * B_LD + kcl * 16;
+    }
+
+    const int wave = tid >> 6, lane = tid & 63;
+    const int hh = lane >> 5, li = lane & 31;
+    const int mb = wave & 3, np = wave >> 2;
+    const int rb0 = GATEUP ? np : 2 * np;
+    const int rb1 = GATEUP ? 2 + np : 2 * np + 1;
+    const bool active = __builtin_amdgcn_readfirstlane(32 * mb < mc ? 1 : 0) != 0;
+    // scales of this lane's two weight rows
+    const int R0 = 32 * rb0 + li, R1 = 32 * rb1 + li;
+    const uint16_t *sp0 = reinterpret_cast<const uint16_t *>(blob + a.s_off + (size_t)s_tile[R0 >> 4] * a.tile_s) + (R0 & 15);
+    const uint16_t *sp1 = reinterpret_cast<const uint16_t *>(blob + a.s_off + (size_t)s_tile[R1 >> 4] * a.tile_s) + (R1 & 15);
+    const int shift = hh ? 0 : 4;
+    const int arow = 32 * mb + li;
+
+    double acc[2][16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            acc[i][r] = 0.0;
+
+    uint4 ra[2], rbv;
+    auto gload = [&](int stage) {
+        const size_t ko = (size_t)stage * KB;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            ra[j] = *reinterpret_cast<const uint4 *>(ga[j] + ko * 32);
+        rbv = *reinterpret_cast<const uint4 *>(gb + ko * 256);
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            *reinterpret_cast<uint4 *>(lds_a + buf * A_STAGE + la[j]) = ra[j];
+        *reinterpret_cast<uint4 *>(lds_b + buf * B_STAGE + lb) = rbv;
+    };
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int st = 0; st < n_stages; ++st) {
+        const int buf = st & 1;
+        if (st + 1 < n_stages)
+            gload(st + 1);
+        if (active) {
+            uint16_t sv0[KB / GS], sv1[KB / GS];
+#pragma unroll
+            for (int u = 0; u < KB / GS; ++u) {
+                sv0[u] = sp0[(size_t)(st * (KB / GS) + u) * 16];
+                sv1[u] = sp1[(size_t)(st * (KB / GS) + u) * 16];
+            }
+            stage_compute<GS>(lds_a + buf * A_STAGE, lds_b + buf * B_STAGE, arow, R0, R1, hh, shift,
+                              sv0, sv1, acc);
+        }
+        if (st + 1 < n_stages)
+            lstore(buf ^ 1);
+        __syncthreads();
+    }
+    if (!active)
+        return;
+
+    // epilogue: register r of lane l holds activation row 8(r/4)+4(l/32)+r%4
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        p0[r] = 0.0;
-        p1[r] = 0.0;
-    }
-    constexpr int U = 4;
-    for (int c0 = 0; c0 < KC; c0 += U) {
-        uint4 av[U], w0[U], w1[U];
-        uint16_t sv0[U / GS], sv1[U / GS];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            av[u] = *reinterpret_cast<const uint4 *>(ap + (size_t)(c0 + u) * 32);
-            w0[u] = *reinterpret_cast<const uint4 *>(b0 + (size_t)(c0 + u) * 256);
-            w1[u] = *reinterpret_cast<const uint4 *>(b1 + (size_t)(c0 + u) * 256);
-        }
-#pragma unroll
-        for (int u = 0; u < U / GS; ++u) {
-            sv0[u] = s0[(size_t)(c0 / GS + u) * 16];
-            sv1[u] = s1[(size_t)(c0 / GS + u) * 16];
-        }
-#pragma unroll
-        for (int u = 0; u < U; u += GS) {
-            v16i d0 = {0}, d1 = {0};
-#pragma unroll
-            for (int v = 0; v < GS; ++v) {
-                v4i A = as_v4i(av[u + v]);
-                d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, nibble_bytes(w0[u + v], shift), d0, 0, 0, 0);
-                d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, nibble_bytes(w1[u + v], shift), d1, 0, 0, 0);
-            }
-            const double sd0 = (double)f16_to_f32(sv0[u / GS]) * 0.0625;
-            const double sd1 = (double)f16_to_f32(sv1[u / GS]) * 0.0625;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                p0[r] = fma((double)d0[r], sd0, p0[r]);
-                p1[r] = fma((double)d1[r], sd1, p1[r]);
-            }
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int tok = 32 * wm + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const int tok = 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);
         const int slot = s_slot[tok];
-        if (slot >= 0) {
-            const double sc = (double)s_sc[tok];
-            float *o = a.out + (size_t)slot * a.ldo;
-            o[n0] = (float)(p0[r] * sc);
-            o[n1] = (float)(p1[r] * sc);
+        if (slot < 0)
+            continue;
+        const double sc = (double)s_sc[tok];
+        float *o = out + (size_t)slot * ldo;
+        if (GATEUP) {
+            const double G = acc[0][r] * sc, U = acc[1][r] * sc;
+            o[64 * nb + 32 * np + li] = (float)(G / (1.0 + exp(-G)) * U);
+        } else {
+            o[128 * nb + 32 * rb0 + li] = (float)(acc[0][r] * sc);
+            o[128 * nb + 32 * rb1 + li] = (float)(acc[1][r] * sc);
         }
     }
 }
@@ -352,22 +369,22 @@ hipError_t launch_gateup_mfma(const ProjArgs &a, const moe_ctx *c, int T, int F,
     const int grid = grid_for(mt_max, F / 64);
     const int2 *tl = reinterpret_cast<const int2 *>(c->tiles);
     if (a.group_shift)
-        gateup_mfma_kernel<2><<<grid, 256, 0, st>>>(a, tl, c->n_tiles, mt_max, F / 64, h, ldh);
+        mfma_proj_kernel<true, 2><<<grid, 512, 0, st>>>(a, tl, c->n_tiles, mt_max, F / 64, h, ldh);
     else
-        gateup_mfma_kernel<1><<<grid, 256, 0, st>>>(a, tl, c->n_tiles, mt_max, F / 64, h, ldh);
+        mfma_proj_kernel<true, 1><<<grid, 512, 0, st>>>(a, tl, c->n_tiles, mt_max, F / 64, h, ldh);
     return hipGetLastError();
 }
 
 hipError_t launch_proj_mfma(const ProjArgs &a, const moe_ctx *c, int T, int n_rows, hipStream_t st)
 {
-    // debug projections use a single blob (one expert holding T rows)
+    // inspection projections use a single blob (one expert holding T rows)
     const int mt_max = (a.ex.E == 0) ? (T + MT - 1) / MT : tiles_bound(c, T);
     const int grid = grid_for(mt_max, n_rows / 128);
     const int2 *tl = reinterpret_cast<const int2 *>(c->tiles);
     if (a.group_shift)
-        proj_mfma_kernel<2><<<grid, 256, 0, st>>>(a, tl, c->n_tiles, mt_max, n_rows / 128);
+        mfma_proj_kernel<false, 2><<<grid, 512, 0, st>>>(a, tl, c->n_tiles, mt_max, n_rows / 128, a.out, a.ldo);
     else
-        proj_mfma_kernel<1><<<grid, 256, 0, st>>>(a, tl, c->n_tiles, mt_max, n_rows / 128);
+        mfma_proj_kernel<false, 1><<<grid, 512, 0, st>>>(a, tl, c->n_tiles, mt_max, n_rows / 128, a.out, a.ldo);
     return hipGetLastError();
 }
 
