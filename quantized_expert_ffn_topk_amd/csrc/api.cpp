@@ -169,6 +169,8 @@ extern "C" moe_status moe_ctx_create(int32_t device, const moe_layer_desc *desc,
     ALLOC(c->active, E + 1);
     ALLOC(c->n_active, 1);
     ALLOC(c->done, 4);
+    ALLOC(c->ctr_gu, E + 1);
+    ALLOC(c->ctr_dn, H / 32);
     ALLOC(c->h, T * S * F);
     ALLOC(c->qh, T * S * F);
     ALLOC(c->sh, T * S);
@@ -191,6 +193,8 @@ extern "C" moe_status moe_ctx_create(int32_t device, const moe_layer_desc *desc,
         (e = hipMemcpy(c->zero1, &zero, 4, hipMemcpyHostToDevice)) != hipSuccess ||
         (e = hipMemcpy(c->one1, &one, 4, hipMemcpyHostToDevice)) != hipSuccess ||
         (e = hipMemset(c->done, 0, 16)) != hipSuccess ||
+        (e = hipMemset(c->ctr_gu, 0, (E + 1) * 4)) != hipSuccess ||
+        (e = hipMemset(c->ctr_dn, 0, (H / 32) * 4)) != hipSuccess ||
         (e = hipMemset(c->n_tiles, 0, 16)) != hipSuccess) {
         ctx_free(c);
         return hip_fail(e, "workspace init");
@@ -309,12 +313,58 @@ extern "C" moe_status moe_ctx_profile_read(moe_ctx *ctx, double *ms, int64_t *co
         prof_end(c, (kind), st);                 \
     } while (0)
 
+// Few tokens on the GEMV path: routing, quantisation and lists in one launch,
+// requant and combine fused into the projections.
+static bool small_path(const moe_ctx *c, int T)
+{
+    // the fused down kernel requantises SwiGLU rows of up to 4096 values
+    // (the fused kernels keep a token's router slice and a SwiGLU row in registers)
+    return T <= RS_MAXT && c->d.wfmt == MOE_WFMT_INT4 && c->d.ffn <= 4096 &&
+           c->d.hidden <= 8192 && !use_mfma(c, T);
+}
+
+static RouteSmallArgs route_small_args(moe_ctx *c, const void *x, int T, const moe_layer_weights *w,
+                                       int32_t *idx, float *gw, int flags)
+{
+    const moe_layer_desc &d = c->d;
+    RouteSmallArgs r{};
+    r.x = static_cast<const uint16_t *>(x);
+    r.T = T;
+    r.H = d.hidden;
+    r.Wr = w ? w->router_w : nullptr;
+    r.bias = w ? w->router_bias : nullptr;
+    r.E = d.n_experts;
+    r.k = d.top_k;
+    r.r = d.routed_scale;
+    r.logits = c->logits;
+    r.idx = idx;
+    r.w = gw;
+    r.flags = flags;
+    r.xq = c->xq;
+    r.sa = c->sa;
+    r.cnt = c->cnt;
+    r.list = c->list;
+    r.list_stride = c->max_tokens;
+    r.active = c->active;
+    r.n_active = c->n_active;
+    r.n_shared = d.n_shared;
+    r.done = c->done;
+    return r;
+}
+
+// Router + top-k.  On the few-token path `extra` (RS_QUANT | RS_LISTS) folds
+// the token quantisation and the routing lists into the same launch.
 static moe_status router_enqueue(moe_ctx *c, const void *x, int32_t T, const moe_layer_weights *w,
-                                 int32_t *idx, float *gw, hipStream_t st)
+                                 int32_t *idx, float *gw, hipStream_t st, int extra = 0)
 {
     if (!w->router_w || !w->router_bias)
         return fail(MOE_E_INVAL, "router weights are NULL");
     const moe_layer_desc &d = c->d;
+    if (small_path(c, T)) {
+        LAUNCH(MOE_PROF_ROUTER, "routing launch",
+               launch_route_small(route_small_args(c, x, T, w, idx, gw, RS_ROUTER | extra), st));
+        return MOE_OK;
+    }
     LAUNCH(MOE_PROF_ROUTER, "router logits launch",
            launch_router_logits(static_cast<const uint16_t *>(x), T, d.hidden, w->router_w,
                                 d.n_experts, c->logits, st));
@@ -352,7 +402,7 @@ static int mg_for(int T)
 
 static moe_status ffn_enqueue(moe_ctx *c, const void *x, int32_t T, const moe_layer_weights *w,
                               const void *const *expert_ptrs, const int32_t *idx,
-                              const float *gw, void *out, hipStream_t st)
+                              const float *gw, void *out, hipStream_t st, bool prepped = false)
 {
     const moe_layer_desc &d = c->d;
     const int H = d.hidden, F = d.ffn, E = d.n_experts, k = d.top_k;
@@ -362,11 +412,32 @@ static moe_status ffn_enqueue(moe_ctx *c, const void *x, int32_t T, const moe_la
         return fail(MOE_E_INVAL, "expert_ptrs is NULL");
     if (d.wfmt == MOE_WFMT_MXFP4)
         return mx_ffn_enqueue(c, x, T, w, expert_ptrs, idx, gw, out, st);
-    LAUNCH(MOE_PROF_QUANT, "quant launch",
-           launch_quant_tokens(static_cast<const uint16_t *>(x), T, H, c->xq, c->sa, st));
-    LAUNCH(MOE_PROF_PERMUTE, "permute launch",
-           launch_permute(idx, T, k, E, d.n_shared, c->cnt, c->list, c->max_tokens, c->active,
-                          c->n_active, c->done, st));
+    const bool small = small_path(c, T);
+    if (small && !prepped) {
+        LAUNCH(MOE_PROF_QUANT, "quant/lists launch",
+               launch_route_small(route_small_args(c, x, T, nullptr, const_cast<int32_t *>(idx),
+                                                   const_cast<float *>(gw), RS_QUANT | RS_LISTS),
+                                  st));
+    } else if (!small) {
+        LAUNCH(MOE_PROF_QUANT, "quant launch",
+               launch_quant_tokens(static_cast<const uint16_t *>(x), T, H, c->xq, c->sa, st));
+        LAUNCH(MOE_PROF_PERMUTE, "permute launch",
+               launch_permute(idx, T, k, E, d.n_shared, c->cnt, c->list, c->max_tokens, c->active,
+                              c->n_active, c->done, st));
+    }
+    TailArgs tail{};
+    tail.qh = c->qh;
+    tail.sh = c->sh;
+    tail.F = F;
+    tail.idx = idx;
+    tail.w = gw;
+    tail.T = T;
+    tail.k = k;
+    tail.E = E;
+    tail.n_shared = d.n_shared;
+    tail.H = H;
+    tail.out_dtype = d.out_dtype;
+    tail.out = out;
     const int max_active = (T * k < E ? T * k : E) + d.n_shared;
     const int mg = mg_for(T);
 
@@ -396,14 +467,17 @@ static moe_status ffn_enqueue(moe_ctx *c, const void *x, int32_t T, const moe_la
         LAUNCH(MOE_PROF_TILES, "tile list launch", launch_mfma_tiles(c, T, st));
         LAUNCH(MOE_PROF_GATEUP, "gate/up launch", launch_gateup_mfma(a, c, T, F, c->h, F, st));
     } else {
+        tail.ctr = c->ctr_gu;
         LAUNCH(MOE_PROF_GATEUP, "gate/up launch",
-               launch_gateup_gemv(a, max_active, F, mg, c->h, F, st));
+               launch_gateup_gemv(a, max_active, F, mg, c->h, F, small ? &tail : nullptr, st));
     }
-    LAUNCH(MOE_PROF_REQUANT, "requant launch",
-           launch_requant(c->h, T * c->S, F, c->qh, c->sh, st));
+    if (!small)
+        LAUNCH(MOE_PROF_REQUANT, "requant launch",
+               launch_requant(c->h, T * c->S, F, c->qh, c->sh, st));
     // down -> Y [T*S, H]
     a.q = c->qh;
     a.s = c->sh;
+    a.hsrc = nullptr;
     a.in_by_token = 0;
     a.K = F;
     a.w_off = c->L.dn_w;
@@ -415,12 +489,15 @@ static moe_status ffn_enqueue(moe_ctx *c, const void *x, int32_t T, const moe_la
     a.j_stride = 1;
     a.out = c->Y;
     a.ldo = H;
+    tail.ctr = c->ctr_dn;
     if (mfma)
         LAUNCH(MOE_PROF_DOWN, "down launch", launch_proj_mfma(a, c, T, H, st));
     else
-        LAUNCH(MOE_PROF_DOWN, "down launch", launch_proj_gemv(a, max_active, H / 32, mg, st));
-    LAUNCH(MOE_PROF_COMBINE, "combine launch",
-           launch_combine(c->Y, idx, gw, T, k, E, d.n_shared, H, out, d.out_dtype, st));
+        LAUNCH(MOE_PROF_DOWN, "down launch",
+               launch_proj_gemv(a, max_active, H / 32, mg, small ? &tail : nullptr, st));
+    if (!small)
+        LAUNCH(MOE_PROF_COMBINE, "combine launch",
+               launch_combine(c->Y, idx, gw, T, k, E, d.n_shared, H, out, d.out_dtype, st));
     return MOE_OK;
 }
 
@@ -459,11 +536,12 @@ extern "C" moe_status moe_layer_forward(moe_ctx *ctx, const void *x, int32_t T,
     int32_t *idx = idx_out ? idx_out : ctx->idx;
     float *gw = gate_w_out ? gate_w_out : ctx->gw;
     ctx->last_T = T;
-    s = router_enqueue(ctx, x, T, w, idx, gw, st);
+    const bool fused = small_path(ctx, T) && ctx->d.wfmt == MOE_WFMT_INT4;
+    s = router_enqueue(ctx, x, T, w, idx, gw, st, fused ? (RS_QUANT | RS_LISTS) : 0);
     if (s)
         return s;
     if (!cache) {
-        s = ffn_enqueue(ctx, x, T, w, w->expert_ptrs, idx, gw, out, st);
+        s = ffn_enqueue(ctx, x, T, w, w->expert_ptrs, idx, gw, out, st, fused);
         if (s)
             return s;
         return prof_collect(ctx);
@@ -473,7 +551,7 @@ extern "C" moe_status moe_layer_forward(moe_ctx *ctx, const void *x, int32_t T,
     if (s)
         return s;
     // the caller may prefetch the next layer now, then calls moe_cache_release
-    s = ffn_enqueue(ctx, x, T, w, table, idx, gw, out, st);
+    s = ffn_enqueue(ctx, x, T, w, table, idx, gw, out, st, fused);
     if (s)
         return s;
     return prof_collect(ctx);
@@ -571,7 +649,7 @@ extern "C" moe_status moe_debug_project(moe_ctx *ctx, const void *blob, int32_t 
             return hip_fail(e, "projection launch");
         return MOE_OK;
     }
-    if ((e = launch_proj_gemv(a, 1, N / 32, mg_for(T), st)) != hipSuccess)
+    if ((e = launch_proj_gemv(a, 1, N / 32, mg_for(T), nullptr, st)) != hipSuccess)
         return hip_fail(e, "projection launch");
     return MOE_OK;
 }

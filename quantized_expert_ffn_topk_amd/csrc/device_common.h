@@ -65,6 +65,50 @@ __device__ __forceinline__ float block_max_256(float v, float *red4)
     return r;
 }
 
+// Cross-block hand-off inside one kernel on a multi-XCD GPU.  Each XCD has its
+// own L2; a device-scope release fence would write the whole L2 back.  Instead,
+// data that another block reads in the same kernel is stored and loaded with
+// relaxed device-scope atomics (they bypass the XCD-local L2), the writer waits
+// until its stores have completed (s_waitcnt), and a device-scope counter then
+// elects the last block, which reads the data with the same atomic loads.
+__device__ __forceinline__ void store_dev(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev(double *p, double v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev(int32_t *p, int32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float *p)
+{
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double load_dev(const double *p)
+{
+    return __hip_atomic_load(const_cast<double *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_dev(const int32_t *p)
+{
+    return __hip_atomic_load(const_cast<int32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// True in every thread of the block that arrives last of `total` at *ctr.
+// Callers store their hand-off data with store_dev first.
+__device__ __forceinline__ bool block_arrives_last(uint32_t *ctr, uint32_t total, int *s_flag)
+{
+    __builtin_amdgcn_s_waitcnt(0);        // this thread's stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *s_flag = (__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   total - 1u) ? 1 : 0;
+    __syncthreads();
+    return *s_flag != 0;
+}
+
 // v_dot4_i32_i8: c + sum of four signed byte products.
 __device__ __forceinline__ int sdot4(int a, int b, int c)
 {

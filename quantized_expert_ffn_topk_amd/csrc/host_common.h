@@ -26,6 +26,7 @@ struct moe_ctx {
     // routing lists
     int32_t *cnt = nullptr, *list = nullptr, *active = nullptr, *n_active = nullptr;
     uint32_t *done = nullptr;
+    uint32_t *ctr_gu = nullptr, *ctr_dn = nullptr;   // fused-tail counters
     // expert FFN intermediates, one row per slot
     float *h = nullptr;
     int8_t *qh = nullptr;

@@ -10,99 +10,162 @@
 // Each int32 group sum times its fp16 scale is exact in fp64 and so is their
 // sum (the packer bounds the scale spread of a row), so the fp64 result does
 // not depend on how lanes and waves split the reduction.
+//
+// Work split: a block (4 waves) owns a pair of 16-row weight tiles of one
+// expert; wave w reads tile w>>1, half w&1 of the K chunks.  Lane l owns row
+// l&15 and every 4th chunk from l>>4, so one 16-byte load per lane reads 1 KiB
+// of contiguous blob (4 chunks x 16 rows).  A wave's first U loads are issued
+// before the activation rows are staged in LDS, so the weight stream starts at
+// once.
+//
+// Fused tails (decode, few tokens): the last block to finish an expert's
+// gate/up requantises that expert's SwiGLU rows; the last block to finish an
+// output tile of the down projection combines the experts for that tile.
+// "Last" is decided with a device-scope counter that the last block resets.
 #include "device_common.h"
-#include "moe_internal.h"
+#include "host_common.h"
 
 namespace moe {
 
-// ---------------------------------------------------------------------------
-// Exact partial sums of a pair of 16-row tiles for up to MG activation rows.
-// Wave w handles tile w>>1 and half w&1 of the K chunks.  Lane l owns row
-// l&15 and every 4th chunk starting at l>>4, so one 16-byte load per lane
-// reads 1 KiB of contiguous blob (4 chunks x 16 rows).  Results go to
-// part[wave][m][r] in LDS.
-// ---------------------------------------------------------------------------
-template <int MG>
-__device__ __forceinline__ void tile_pair_partials(const uint8_t *__restrict__ wt0,
-                                                   const uint8_t *__restrict__ wt1,
-                                                   const uint16_t *__restrict__ st0,
-                                                   const uint16_t *__restrict__ st1, int KC,
-                                                   int gshift, int mc,
-                                                   const int8_t *__restrict__ lq, int K,
-                                                   double *__restrict__ part)
+template <int U>
+__device__ __forceinline__ void load_batch(const uint8_t *__restrict__ wt,
+                                           const uint16_t *__restrict__ st, int cb, int it0,
+                                           int niter, int c4, int r, int gshift, uint4 (&wv)[U],
+                                           uint16_t (&sv)[U])
 {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int j = wave >> 1, half = wave & 1;
-    const uint8_t *wt = j ? wt1 : wt0;
-    const uint16_t *st = j ? st1 : st0;
-    const int r = lane & 15, c4 = lane >> 4;
-    const int nk = KC >> 1;
-    const int cb = half * nk;
-    const int niter = nk >> 2;
-    double p[MG];
 #pragma unroll
-    for (int m = 0; m < MG; ++m)
-        p[m] = 0.0;
-    constexpr int U = 8;
-    for (int it0 = 0; it0 < niter; it0 += U) {
-        uint4 wv[U];
-        uint16_t sv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (it0 + u < niter) {
-                int c = cb + (it0 + u) * 4 + c4;
-                wv[u] = *reinterpret_cast<const uint4 *>(wt + ((size_t)c * 16 + r) * 16);
-                sv[u] = st[(size_t)(c >> gshift) * 16 + r];
-            }
+    for (int u = 0; u < U; ++u) {
+        if (it0 + u < niter) {
+            const int c = cb + (it0 + u) * 4 + c4;
+            wv[u] = *reinterpret_cast<const uint4 *>(wt + ((size_t)c * 16 + r) * 16);
+            sv[u] = st[(size_t)(c >> gshift) * 16 + r];
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (it0 + u < niter) {
-                int c = cb + (it0 + u) * 4 + c4;
-                double sd = (double)f16_to_f32(sv[u]) * 0.0625;
-                uint32_t wd[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
-                int lo[4], hi[4];
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    lo[d] = (int)((wd[d] << 4) & 0xf0f0f0f0u);
-                    hi[d] = (int)(wd[d] & 0xf0f0f0f0u);
-                }
-#pragma unroll
-                for (int m = 0; m < MG; ++m) {
-                    if (m < mc) {
-                        const int4 *qa = reinterpret_cast<const int4 *>(lq + m * K + c * 32);
-                        int4 a0 = qa[0], a1 = qa[1];
-                        int acc = 0;
-                        acc = sdot4(lo[0], a0.x, acc);
-                        acc = sdot4(lo[1], a0.y, acc);
-                        acc = sdot4(lo[2], a0.z, acc);
-                        acc = sdot4(lo[3], a0.w, acc);
-                        acc = sdot4(hi[0], a1.x, acc);
-                        acc = sdot4(hi[1], a1.y, acc);
-                        acc = sdot4(hi[2], a1.z, acc);
-                        acc = sdot4(hi[3], a1.w, acc);
-                        p[m] = fma((double)acc, sd, p[m]);
-                    }
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int m = 0; m < MG; ++m) {
-        p[m] += shfl_xor_d(p[m], 16);
-        p[m] += shfl_xor_d(p[m], 32);
-    }
-    if (c4 == 0) {
-#pragma unroll
-        for (int m = 0; m < MG; ++m)
-            part[(wave * MG + m) * 16 + r] = p[m];
     }
 }
 
-template <int MG>
-__device__ __forceinline__ size_t gemv_lds_bytes(int K)
+template <int MG, int U>
+__device__ __forceinline__ void compute_batch(const uint4 (&wv)[U], const uint16_t (&sv)[U], int cb,
+                                              int it0, int niter, int c4, int mc,
+                                              const int8_t *__restrict__ lq, int K, double (&p)[MG])
 {
-    return (size_t)MG * K + 4 * MG * 16 * 8 + MG * 8;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (it0 + u < niter) {
+            const int c = cb + (it0 + u) * 4 + c4;
+            const double sd = (double)f16_to_f32(sv[u]) * 0.0625;
+            const uint32_t wd[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+            int lo[4], hi[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                lo[d] = (int)((wd[d] << 4) & 0xf0f0f0f0u);
+                hi[d] = (int)(wd[d] & 0xf0f0f0f0u);
+            }
+#pragma unroll
+            for (int m = 0; m < MG; ++m) {
+                if (m < mc) {
+                    const int4 *qa = reinterpret_cast<const int4 *>(lq + m * K + c * 32);
+                    const int4 a0 = qa[0], a1 = qa[1];
+                    int acc = 0;
+                    acc = sdot4(lo[0], a0.x, acc);
+                    acc = sdot4(lo[1], a0.y, acc);
+                    acc = sdot4(lo[2], a0.z, acc);
+                    acc = sdot4(lo[3], a0.w, acc);
+                    acc = sdot4(hi[0], a1.x, acc);
+                    acc = sdot4(hi[1], a1.y, acc);
+                    acc = sdot4(hi[2], a1.z, acc);
+                    acc = sdot4(hi[3], a1.w, acc);
+                    p[m] = fma((double)acc, sd, p[m]);
+                }
+            }
+        }
+    }
+}
+
+// Requantises one fp32 row (K <= 4096) into LDS codes with the token
+// quantisation rule; block column 0 also writes codes and scale to global.
+__device__ __forceinline__ void requant_stage(const float *__restrict__ hr, int K, int8_t *lq,
+                                              float *ls, int8_t *gq, float *gs, bool store)
+{
+    __shared__ float red[4];
+    float v[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int i = threadIdx.x * 4 + 1024 * j;
+        if (i < K) {
+            const float4 f = *reinterpret_cast<const float4 *>(hr + i);
+            v[4 * j] = f.x;
+            v[4 * j + 1] = f.y;
+            v[4 * j + 2] = f.z;
+            v[4 * j + 3] = f.w;
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
+        }
+    }
+    amax = block_max_256(amax, red);
+    float inv = 0.0f, sc = 0.0f;
+    if (amax > 0.0f) {
+        inv = 127.0f / amax;
+        sc = amax / 127.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int i = threadIdx.x * 4 + 1024 * j;
+        if (i < K) {
+            uint32_t packed = 0u;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float rr = fminf(fmaxf(rintf(v[4 * j + b] * inv), -127.0f), 127.0f);
+                packed |= ((uint32_t)(int)rr & 0xffu) << (8 * b);
+            }
+            *reinterpret_cast<uint32_t *>(lq + i) = packed;
+            if (store)
+                *reinterpret_cast<uint32_t *>(gq + i) = packed;
+        }
+    }
+    if (threadIdx.x == 0) {
+        *ls = sc;
+        if (store)
+            *gs = sc;
+    }
+}
+
+// Requantises one row of F <= 4096 floats written by other blocks of this
+// kernel (store_dev): all of the thread's loads are issued before any is used.
+__device__ __forceinline__ void requant_row_dev(const float *__restrict__ hr, int F,
+                                                int8_t *__restrict__ qr, float *__restrict__ s_out,
+                                                float *red)
+{
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int i = threadIdx.x * 4 + 1024 * (j >> 2) + (j & 3);
+        v[j] = (i < F) ? load_dev(hr + i) : 0.0f;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        amax = fmaxf(amax, fabsf(v[j]));
+    amax = block_max_256(amax, red);
+    float inv = 0.0f, sc = 0.0f;
+    if (amax > 0.0f) {
+        inv = 127.0f / amax;
+        sc = amax / 127.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int i = threadIdx.x * 4 + 1024 * j;
+        if (i < F) {
+            uint32_t packed = 0u;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float rr = fminf(fmaxf(rintf(v[4 * j + b] * inv), -127.0f), 127.0f);
+                packed |= ((uint32_t)(int)rr & 0xffu) << (8 * b);
+            }
+            *reinterpret_cast<uint32_t *>(qr + i) = packed;
+        }
+    }
+    if (threadIdx.x == 0)
+        *s_out = sc;
 }
 
 // Stages up to MG activation rows of the expert's list into LDS.
@@ -112,17 +175,119 @@ __device__ __forceinline__ void stage_rows(const ProjArgs &a, const int32_t *lst
 {
     const int K = a.K;
     for (int m = 0; m < mc; ++m) {
-        int slot = lst[base + m];
-        int row = a.in_by_token ? slot / a.rt.S : slot;
-        const uint4 *src = reinterpret_cast<const uint4 *>(a.q + (size_t)row * K);
-        uint4 *dst = reinterpret_cast<uint4 *>(lq + m * K);
-        for (int i = threadIdx.x; i < K / 16; i += 256)
-            dst[i] = src[i];
-        if (threadIdx.x == 0) {
-            lsa[m] = a.s[row];
-            lslot[m] = slot;
+        const int slot = lst[base + m];
+        const int row = a.in_by_token ? slot / a.rt.S : slot;
+        if (a.hsrc) {
+            requant_stage(a.hsrc + (size_t)row * K, K, lq + m * K, lsa + m,
+                          const_cast<int8_t *>(a.q) + (size_t)row * K, const_cast<float *>(a.s) + row,
+                          blockIdx.y == 0);
+        } else {
+            const uint4 *src = reinterpret_cast<const uint4 *>(a.q + (size_t)row * K);
+            uint4 *dst = reinterpret_cast<uint4 *>(lq + m * K);
+            for (int i = threadIdx.x; i < K / 16; i += 256)
+                dst[i] = src[i];
+            if (threadIdx.x == 0)
+                lsa[m] = a.s[row];
         }
+        if (threadIdx.x == 0)
+            lslot[m] = slot;
     }
+}
+
+// Exact partial sums of tile pair (wt0, wt1) for all passes of MG rows; calls
+// epi(base, mc, part, lsa, lslot) after each pass (part[wave][m][r] in LDS).
+template <int MG, int U, class Epi>
+__device__ __forceinline__ void gemv_tile_pair(const ProjArgs &a, const uint8_t *wt0,
+                                               const uint8_t *wt1, const uint16_t *st0,
+                                               const uint16_t *st1, const int32_t *lst, int n,
+                                               unsigned char *smem, Epi epi)
+{
+    const int K = a.K, KC = K >> 5;
+    int8_t *lq = reinterpret_cast<int8_t *>(smem);
+    double *part = reinterpret_cast<double *>(smem + MG * K);
+    float *lsa = reinterpret_cast<float *>(part + 4 * MG * 16);
+    int *lslot = reinterpret_cast<int *>(lsa + MG);
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int j = wave >> 1, half = wave & 1;
+    const uint8_t *wt = j ? wt1 : wt0;
+    const uint16_t *st = j ? st1 : st0;
+    const int r = lane & 15, c4 = lane >> 4;
+    const int nk = KC >> 1;
+    const int cb = half * nk;
+    const int niter = nk >> 2;
+
+    uint4 wv[U];
+    uint16_t sv[U];
+    load_batch<U>(wt, st, cb, 0, niter, c4, r, a.group_shift, wv, sv);   // before staging
+    for (int base = 0; base < n; base += MG) {
+        const int mc = min(MG, n - base);
+        stage_rows<MG>(a, lst, base, mc, lq, lsa, lslot);
+        __syncthreads();
+        double p[MG];
+#pragma unroll
+        for (int m = 0; m < MG; ++m)
+            p[m] = 0.0;
+        for (int it0 = 0; it0 < niter; it0 += U) {
+            if (base > 0 || it0 > 0)
+                load_batch<U>(wt, st, cb, it0, niter, c4, r, a.group_shift, wv, sv);
+            compute_batch<MG, U>(wv, sv, cb, it0, niter, c4, mc, lq, K, p);
+        }
+#pragma unroll
+        for (int m = 0; m < MG; ++m) {
+            p[m] += shfl_xor_d(p[m], 16);
+            p[m] += shfl_xor_d(p[m], 32);
+        }
+        if (c4 == 0) {
+#pragma unroll
+            for (int m = 0; m < MG; ++m)
+                part[(wave * MG + m) * 16 + r] = p[m];
+        }
+        __syncthreads();
+        epi(base, mc, part, lsa, lslot);
+        __syncthreads();
+    }
+}
+
+// Requantises one row of F floats into int8 with the token-quantisation rule
+// (DEV: the row was written by other blocks of this kernel with store_dev).
+template <bool DEV>
+__device__ __forceinline__ float4 load4(const float *p)
+{
+    if (DEV)
+        return make_float4(load_dev(p), load_dev(p + 1), load_dev(p + 2), load_dev(p + 3));
+    return *reinterpret_cast<const float4 *>(p);
+}
+
+template <bool DEV>
+__device__ __forceinline__ void requant_row(const float *__restrict__ hr, int F,
+                                            int8_t *__restrict__ qr, float *__restrict__ s_out,
+                                            float *red)
+{
+    float amax = 0.0f;
+    for (int i = threadIdx.x * 4; i < F; i += 1024) {
+        const float4 v = load4<DEV>(hr + i);
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+    amax = block_max_256(amax, red);
+    float inv = 0.0f, sc = 0.0f;
+    if (amax > 0.0f) {
+        inv = 127.0f / amax;
+        sc = amax / 127.0f;
+    }
+    for (int i = threadIdx.x * 4; i < F; i += 1024) {
+        const float4 v = load4<DEV>(hr + i);
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+        uint32_t packed = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float rr = fminf(fmaxf(rintf(vv[j] * inv), -127.0f), 127.0f);
+            packed |= ((uint32_t)(int)rr & 0xffu) << (8 * j);
+        }
+        *reinterpret_cast<uint32_t *>(qr + i) = packed;
+    }
+    if (threadIdx.x == 0)
+        *s_out = sc;
 }
 
 // ---------------------------------------------------------------------------
@@ -132,9 +297,9 @@ __device__ __forceinline__ void stage_rows(const ProjArgs &a, const int32_t *lst
 // SwiGLU is the reading taken for the experts' activation (the pages do not
 // name one; DeepSeek-V3-family experts use it).
 // ---------------------------------------------------------------------------
-template <int MG>
+template <int MG, int U, bool TAIL>
 __global__ __launch_bounds__(256) void gateup_gemv_kernel(ProjArgs a, float *__restrict__ h,
-                                                          int ldh)
+                                                          int ldh, TailArgs t)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     const int ai = blockIdx.x;
@@ -144,78 +309,111 @@ __global__ __launch_bounds__(256) void gateup_gemv_kernel(ProjArgs a, float *__r
     const uint8_t *blob =
         reinterpret_cast<const uint8_t *>((e == a.ex.E) ? a.ex.shared : a.ex.ptrs[e]);
     const int b = blockIdx.y;
-    const int K = a.K, KC = K >> 5;
     const uint8_t *wt0 = blob + a.w_off + (size_t)(2 * b) * a.tile_w;
     const uint8_t *wt1 = wt0 + a.tile_w;
-    const uint16_t *st0 =
-        reinterpret_cast<const uint16_t *>(blob + a.s_off + (size_t)(2 * b) * a.tile_s);
+    const uint16_t *st0 = reinterpret_cast<const uint16_t *>(blob + a.s_off + (size_t)(2 * b) * a.tile_s);
     const uint16_t *st1 = reinterpret_cast<const uint16_t *>(blob + a.s_off + (size_t)(2 * b + 1) * a.tile_s);
-    int8_t *lq = reinterpret_cast<int8_t *>(smem);
-    double *part = reinterpret_cast<double *>(smem + MG * K);
-    float *lsa = reinterpret_cast<float *>(part + 4 * MG * 16);
-    int *lslot = reinterpret_cast<int *>(lsa + MG);
     const int n = a.rt.cnt[e];
     const int32_t *lst = a.rt.list + (size_t)e * a.rt.list_stride;
-    for (int base = 0; base < n; base += MG) {
-        const int mc = min(MG, n - base);
-        stage_rows<MG>(a, lst, base, mc, lq, lsa, lslot);
-        __syncthreads();
-        tile_pair_partials<MG>(wt0, wt1, st0, st1, KC, a.group_shift, mc, lq, K, part);
-        __syncthreads();
-        if (threadIdx.x < 16 * mc) {
-            const int m = threadIdx.x >> 4, rr = threadIdx.x & 15;
-            const double sa = (double)lsa[m];
-            double G = (part[(0 * MG + m) * 16 + rr] + part[(1 * MG + m) * 16 + rr]) * sa;
-            double U = (part[(2 * MG + m) * 16 + rr] + part[(3 * MG + m) * 16 + rr]) * sa;
-            double silu = G / (1.0 + exp(-G));
-            h[(size_t)lslot[m] * ldh + 16 * b + rr] = (float)(silu * U);
-        }
-        __syncthreads();
+    gemv_tile_pair<MG, U>(a, wt0, wt1, st0, st1, lst, n, smem,
+                          [&](int, int mc, const double *part, const float *lsa, const int *lslot) {
+                              if (threadIdx.x < 16 * mc) {
+                                  const int m = threadIdx.x >> 4, rr = threadIdx.x & 15;
+                                  const double sa = (double)lsa[m];
+                                  const double G = (part[(0 * MG + m) * 16 + rr] + part[(1 * MG + m) * 16 + rr]) * sa;
+                                  const double Uv = (part[(2 * MG + m) * 16 + rr] + part[(3 * MG + m) * 16 + rr]) * sa;
+                                  const double silu = G / (1.0 + exp(-G));
+                                  float *hp = h + (size_t)lslot[m] * ldh + 16 * b + rr;
+                                  if (TAIL)
+                                      store_dev(hp, (float)(silu * Uv));
+                                  else
+                                      *hp = (float)(silu * Uv);
+                              }
+                          });
+    if (!TAIL)
+        return;
+    __shared__ int s_flag;
+    __shared__ float red[4];
+    if (!block_arrives_last(t.ctr + ai, gridDim.y, &s_flag))
+        return;
+    for (int m = 0; m < n; ++m) {
+        const int slot = lst[m];
+        requant_row_dev(h + (size_t)slot * ldh, t.F, t.qh + (size_t)slot * t.F, t.sh + slot, red);
     }
+    if (threadIdx.x == 0)
+        t.ctr[ai] = 0u;
 }
 
 // ---------------------------------------------------------------------------
 // Plain projection of a pair of tiles (down projection, or one part of the
 // gate/up section): y = fp32(exact sum * row scale) into
-// out[slot*ldo + 32*pair + 16*j + r].
+// out[slot*ldo + 32*pair + 16*j + r].  With TAIL, the last block of output
+// tile `pair` combines: out[t, n] = Y_shared + sum_i w_i * Y_i (fp64, shared
+// first then rank order, rounded once).
 // ---------------------------------------------------------------------------
-template <int MG>
-__global__ __launch_bounds__(256) void proj_gemv_kernel(ProjArgs a)
+template <int MG, int U, bool TAIL>
+__global__ __launch_bounds__(256) void proj_gemv_kernel(ProjArgs a, TailArgs t)
 {
     extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int s_flag;
     const int ai = blockIdx.x;
-    if (ai >= *a.rt.n_active)
+    const int n_act = *a.rt.n_active;
+    if (ai >= n_act)
         return;
     const int e = a.rt.active[ai];
     const uint8_t *blob =
         reinterpret_cast<const uint8_t *>((e == a.ex.E) ? a.ex.shared : a.ex.ptrs[e]);
     const int p = blockIdx.y;
-    const int K = a.K, KC = K >> 5;
     const int tile0 = a.tile_base + p * a.pair_stride, tile1 = tile0 + a.j_stride;
     const uint8_t *wt0 = blob + a.w_off + (size_t)tile0 * a.tile_w;
     const uint8_t *wt1 = blob + a.w_off + (size_t)tile1 * a.tile_w;
     const uint16_t *st0 = reinterpret_cast<const uint16_t *>(blob + a.s_off + (size_t)tile0 * a.tile_s);
     const uint16_t *st1 = reinterpret_cast<const uint16_t *>(blob + a.s_off + (size_t)tile1 * a.tile_s);
-    int8_t *lq = reinterpret_cast<int8_t *>(smem);
-    double *part = reinterpret_cast<double *>(smem + MG * K);
-    float *lsa = reinterpret_cast<float *>(part + 4 * MG * 16);
-    int *lslot = reinterpret_cast<int *>(lsa + MG);
     const int n = a.rt.cnt[e];
     const int32_t *lst = a.rt.list + (size_t)e * a.rt.list_stride;
-    for (int base = 0; base < n; base += MG) {
-        const int mc = min(MG, n - base);
-        stage_rows<MG>(a, lst, base, mc, lq, lsa, lslot);
-        __syncthreads();
-        tile_pair_partials<MG>(wt0, wt1, st0, st1, KC, a.group_shift, mc, lq, K, part);
-        __syncthreads();
-        if (threadIdx.x < 32 * mc) {
-            const int m = threadIdx.x >> 5, j = (threadIdx.x >> 4) & 1, rr = threadIdx.x & 15;
-            double y = (part[((2 * j) * MG + m) * 16 + rr] + part[((2 * j + 1) * MG + m) * 16 + rr]) *
-                       (double)lsa[m];
-            a.out[(size_t)lslot[m] * a.ldo + 32 * p + 16 * j + rr] = (float)y;
+    gemv_tile_pair<MG, U>(a, wt0, wt1, st0, st1, lst, n, smem,
+                          [&](int, int mc, const double *part, const float *lsa, const int *lslot) {
+                              if (threadIdx.x < 32 * mc) {
+                                  const int m = threadIdx.x >> 5, j = (threadIdx.x >> 4) & 1, rr = threadIdx.x & 15;
+                                  const double y = (part[((2 * j) * MG + m) * 16 + rr] + part[((2 * j + 1) * MG + m) * 16 + rr]) *
+                                                   (double)lsa[m];
+                                  float *yp = a.out + (size_t)lslot[m] * a.ldo + 32 * p + 16 * j + rr;
+                                  if (TAIL)
+                                      store_dev(yp, (float)y);
+                                  else
+                                      *yp = (float)y;
+                              }
+                          });
+    if (!TAIL)
+        return;
+    if (!block_arrives_last(t.ctr + p, (uint32_t)n_act, &s_flag))
+        return;
+    const int S = t.k + t.n_shared;
+    for (int q = threadIdx.x; q < t.T * 32; q += 256) {
+        const int tok = q >> 5, col = 32 * p + (q & 31);
+        const float *yt = a.out + (size_t)tok * S * t.H;
+        float y[17];
+#pragma unroll
+        for (int i = 0; i < 17; ++i)               // all loads in flight at once
+            if (i < S)
+                y[i] = load_dev(yt + (size_t)i * t.H + col);
+        double o = t.n_shared ? (double)y[t.k] : 0.0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (i < t.k) {
+                const int ex = t.idx[(size_t)tok * t.k + i];
+                if (ex >= 0 && ex < t.E)
+                    o = fma((double)t.w[(size_t)tok * t.k + i], (double)y[i], o);
+            }
         }
-        __syncthreads();
+        const float f = (float)o;
+        if (t.out_dtype == MOE_DT_BF16)
+            reinterpret_cast<uint16_t *>(t.out)[(size_t)tok * t.H + col] = f32_to_bf16(f);
+        else
+            reinterpret_cast<float *>(t.out)[(size_t)tok * t.H + col] = f;
     }
+    if (threadIdx.x == 0)
+        t.ctr[p] = 0u;
 }
 
 static size_t lds_bytes(int mg, int K)
@@ -230,39 +428,70 @@ static int pick_mg(int mg, int K)
     return mg;
 }
 
-hipError_t launch_gateup_gemv(const ProjArgs &a, int max_active, int F, int mg, float *h,
-                              int ldh, hipStream_t st)
+template <int MG, bool TAIL>
+static void launch_gateup_u(const ProjArgs &a, dim3 grid, size_t lds, float *h, int ldh,
+                            const TailArgs &t, int niter, hipStream_t st)
+{
+    // 12 loads of 16 B per lane per batch measured best on the GLM-shaped
+    // decode layer (24: fewer, larger batches oversubscribe HBM; 8: too few)
+    (void)niter;
+    gateup_gemv_kernel<MG, 12, TAIL><<<grid, 256, lds, st>>>(a, h, ldh, t);
+}
+
+template <int MG, bool TAIL>
+static void launch_proj_u(const ProjArgs &a, dim3 grid, size_t lds, const TailArgs &t, int niter,
+                          hipStream_t st)
+{
+    (void)niter;
+    proj_gemv_kernel<MG, 12, TAIL><<<grid, 256, lds, st>>>(a, t);
+}
+
+hipError_t launch_gateup_gemv(const ProjArgs &a, int max_active, int F, int mg, float *h, int ldh,
+                              const TailArgs *tail, hipStream_t st)
 {
     mg = pick_mg(mg, a.K);
-    dim3 grid(max_active, F / 16);
-    size_t lds = lds_bytes(mg, a.K);
+    const dim3 grid(max_active, F / 16);
+    const size_t lds = lds_bytes(mg, a.K);
+    const int niter = a.K / 256;
+    TailArgs t = tail ? *tail : TailArgs{};
+    const bool fuse = tail != nullptr;
+#define GU(M)                                                              \
+    (fuse ? launch_gateup_u<M, true>(a, grid, lds, h, ldh, t, niter, st)   \
+          : launch_gateup_u<M, false>(a, grid, lds, h, ldh, t, niter, st))
     switch (mg) {
-    case 1: gateup_gemv_kernel<1><<<grid, 256, lds, st>>>(a, h, ldh); break;
-    case 2: gateup_gemv_kernel<2><<<grid, 256, lds, st>>>(a, h, ldh); break;
-    case 4: gateup_gemv_kernel<4><<<grid, 256, lds, st>>>(a, h, ldh); break;
-    default: gateup_gemv_kernel<8><<<grid, 256, lds, st>>>(a, h, ldh); break;
+    case 1: GU(1); break;
+    case 2: GU(2); break;
+    case 4: GU(4); break;
+    default: GU(8); break;
     }
+#undef GU
     return hipGetLastError();
 }
 
 hipError_t launch_proj_gemv(const ProjArgs &a, int max_active, int n_pairs, int mg,
-                            hipStream_t st)
+                            const TailArgs *tail, hipStream_t st)
 {
     mg = pick_mg(mg, a.K);
-    dim3 grid(max_active, n_pairs);
-    size_t lds = lds_bytes(mg, a.K);
+    const dim3 grid(max_active, n_pairs);
+    const size_t lds = lds_bytes(mg, a.K);
+    const int niter = a.K / 256;
+    TailArgs t = tail ? *tail : TailArgs{};
+    const bool fuse = tail != nullptr;
+#define PJ(M) (fuse ? launch_proj_u<M, true>(a, grid, lds, t, niter, st) \
+                    : launch_proj_u<M, false>(a, grid, lds, t, niter, st))
     switch (mg) {
-    case 1: proj_gemv_kernel<1><<<grid, 256, lds, st>>>(a); break;
-    case 2: proj_gemv_kernel<2><<<grid, 256, lds, st>>>(a); break;
-    case 4: proj_gemv_kernel<4><<<grid, 256, lds, st>>>(a); break;
-    default: proj_gemv_kernel<8><<<grid, 256, lds, st>>>(a); break;
+    case 1: PJ(1); break;
+    case 2: PJ(2); break;
+    case 4: PJ(4); break;
+    default: PJ(8); break;
     }
+#undef PJ
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // Requantisation of each SwiGLU row (one per token and expert) to int8, same
-// rule as the token quantisation.
+// rule as the token quantisation (many-token path).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void requant_kernel(const float *__restrict__ h, int F,
                                                       int8_t *__restrict__ q,
@@ -270,35 +499,7 @@ __global__ __launch_bounds__(256) void requant_kernel(const float *__restrict__ 
 {
     __shared__ float red[4];
     const int row = blockIdx.x;
-    const float *hr = h + (size_t)row * F;
-    float amax = 0.0f;
-    for (int i = threadIdx.x * 4; i < F; i += 1024) {
-        float4 v = *reinterpret_cast<const float4 *>(hr + i);
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-    }
-    amax = block_max_256(amax, red);
-    float inv = 0.0f, sc = 0.0f;
-    if (amax > 0.0f) {
-        inv = 127.0f / amax;
-        sc = amax / 127.0f;
-    }
-    int8_t *qr = q + (size_t)row * F;
-    for (int i = threadIdx.x * 8; i < F; i += 2048) {
-        float4 v0 = *reinterpret_cast<const float4 *>(hr + i);
-        float4 v1 = *reinterpret_cast<const float4 *>(hr + i + 4);
-        float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float r = rintf(vv[j] * inv);
-            r = fminf(fmaxf(r, -127.0f), 127.0f);
-            int qi = (int)r;
-            packed[j >> 2] |= ((uint32_t)qi & 0xffu) << (8 * (j & 3));
-        }
-        *reinterpret_cast<uint2 *>(qr + i) = make_uint2(packed[0], packed[1]);
-    }
-    if (threadIdx.x == 0)
-        s[row] = sc;
+    requant_row<false>(h + (size_t)row * F, F, q + (size_t)row * F, s + row, red);
 }
 
 hipError_t launch_requant(const float *h, int rows, int F, int8_t *q, float *s, hipStream_t st)
@@ -310,8 +511,8 @@ hipError_t launch_requant(const float *h, int rows, int F, int8_t *q, float *s, 
 }
 
 // ---------------------------------------------------------------------------
-// Combine: out[t,n] = Y_shared + sum_i w_i * Y_i in fp64, shared first then
-// rank order, rounded once (fp32, or bf16 from that fp32).
+// Combine (many-token path): out[t,n] = Y_shared + sum_i w_i * Y_i in fp64,
+// shared first then rank order, rounded once (fp32, or bf16 from that fp32).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ Y,
                                                       const int32_t *__restrict__ idx,
@@ -327,11 +528,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     const float *yt = Y + (size_t)t * S * H;
     double o = n_shared ? (double)yt[(size_t)k * H + n] : 0.0;
     for (int i = 0; i < k; ++i) {
-        int e = idx[(size_t)t * k + i];
+        const int e = idx[(size_t)t * k + i];
         if (e >= 0 && e < E)
             o = fma((double)w[(size_t)t * k + i], (double)yt[(size_t)i * H + n], o);
     }
-    float f = (float)o;
+    const float f = (float)o;
     if (out_dtype == MOE_DT_BF16)
         reinterpret_cast<uint16_t *>(out)[(size_t)t * H + n] = f32_to_bf16(f);
     else

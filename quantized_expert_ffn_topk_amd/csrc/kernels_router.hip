@@ -312,21 +312,15 @@ __global__ __launch_bounds__(256) void permute_kernel(const int32_t *__restrict_
             mine[t] = t * S + k;
         total = T;
     }
-    if (threadIdx.x == 0) {
-        cnt[e] = total < list_stride ? total : list_stride;
-        __threadfence();
-        unsigned prev = atomicAdd(done, 1u);
-        last = (prev == gridDim.x - 1) ? 1 : 0;
-    }
-    __syncthreads();
-    if (!last || wave != 0)
+    if (threadIdx.x == 0)
+        store_dev(cnt + e, total < list_stride ? total : list_stride);
+    if (!block_arrives_last(done, gridDim.x, &last) || wave != 0)
         return;
-    __threadfence();
     const int nE = gridDim.x;
     int na = 0;
     for (int e0 = 0; e0 < nE; e0 += 64) {
         int ee = e0 + lane;
-        int c = (ee < nE) ? __atomic_load_n(&cnt[ee], __ATOMIC_RELAXED) : 0;
+        int c = (ee < nE) ? load_dev(cnt + ee) : 0;
         uint64_t bal = __ballot(c > 0);
         if (c > 0)
             active[na + __popcll(bal & ((1ull << lane) - 1ull))] = ee;
@@ -377,6 +371,268 @@ hipError_t launch_table_update(const void **table, int set_idx, const void *ptr,
                                hipStream_t st)
 {
     table_update_kernel<<<1, 1, 0, st>>>(table, set_idx, ptr, clear_idx);
+    return hipGetLastError();
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Few-token routing in one launch (decode).  With RS_ROUTER, block e computes
+// the fp64 logits of expert e for all T tokens (each thread a fixed slice of
+// H, then a fixed-order block reduction); the last block to finish then runs
+// the per-token top-k.  The same last block (or the single block when the
+// router is not part of the call) quantises the tokens and builds the routing
+// lists: per expert its slots in token order, the shared expert's slots, and
+// the list of experts with rows.
+// ---------------------------------------------------------------------------
+// Top-k of one token by ranks: every thread takes experts e = tid + 256j and
+// counts the experts that precede e in the order (c desc, index asc); experts
+// with rank < k are the selection, in rank order.  s_c/s_s: LDS scratch of E
+// doubles each; sel_s: k doubles.
+__device__ __forceinline__ void topk_rank_block(const double *__restrict__ lg,
+                                                const float *__restrict__ bias, int E, int k,
+                                                float r, int32_t *__restrict__ idx_out,
+                                                float *__restrict__ w_out, int32_t *s_idx,
+                                                double *s_c, double *s_s, double *sel_s)
+{
+    for (int e = threadIdx.x; e < E; e += 256) {
+        const double sv = 1.0 / (1.0 + exp(-load_dev(lg + e)));
+        const double cv = sv + (double)bias[e];
+        s_s[e] = sv;
+        s_c[e] = (cv != cv) ? -INFINITY : cv;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) {
+        const double ce = s_c[e];
+        int rank = 0;
+#pragma unroll 16
+        for (int f = 0; f < E; ++f) {
+            const double cf = s_c[f];
+            rank += (cf > ce || (cf == ce && f < e)) ? 1 : 0;
+        }
+        if (rank < k) {
+            s_idx[rank] = e;
+            sel_s[rank] = s_s[e];
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double den = 0.0;
+        for (int i = 0; i < k; ++i)
+            den += sel_s[i];
+        for (int i = 0; i < k; ++i) {
+            const double wi = (den > 0.0) ? (sel_s[i] / den) * (double)r : 0.0;
+            idx_out[i] = s_idx[i];
+            w_out[i] = (float)wi;
+        }
+    }
+    __syncthreads();
+}
+
+// Per-token int8 quantisation of T rows by one block (same rule as
+// quant_tokens_kernel).
+__device__ __noinline__ void quant_rows_block(const uint16_t *__restrict__ x, int T, int H,
+                                              int8_t *__restrict__ xq, float *__restrict__ sa,
+                                              float *red)
+{
+    const int tid = threadIdx.x;
+    for (int m = 0; m < T; ++m) {
+        const uint16_t *xr = x + (size_t)m * H;
+        float amax = 0.0f;
+        for (int i = tid * 8; i < H; i += 2048) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(xr + i);
+            const uint32_t ww[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                amax = fmaxf(amax, fabsf(bf16_to_f32(ww[j] & 0xffffu)));
+                amax = fmaxf(amax, fabsf(bf16_to_f32(ww[j] >> 16)));
+            }
+        }
+        amax = block_max_256(amax, red);
+        float inv = 0.0f, sc = 0.0f;
+        if (amax > 0.0f) {
+            inv = 127.0f / amax;
+            sc = amax / 127.0f;
+        }
+        int8_t *qr = xq + (size_t)m * H;
+        for (int i = tid * 8; i < H; i += 2048) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(xr + i);
+            const uint32_t ww[4] = {v.x, v.y, v.z, v.w};
+            uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float xv = bf16_to_f32((j & 1) ? (ww[j >> 1] >> 16) : (ww[j >> 1] & 0xffffu));
+                const float rr = fminf(fmaxf(rintf(xv * inv), -127.0f), 127.0f);
+                packed[j >> 2] |= ((uint32_t)(int)rr & 0xffu) << (8 * (j & 3));
+            }
+            *reinterpret_cast<uint2 *>(qr + i) = make_uint2(packed[0], packed[1]);
+        }
+        if (tid == 0)
+            sa[m] = sc;
+    }
+}
+
+__global__ __launch_bounds__(256) void route_small_kernel(RouteSmallArgs a)
+{
+    __shared__ double sred[4][RS_MAXT];
+    __shared__ int32_t s_idx[RS_MAXT * 16];
+    __shared__ double s_c[1024], s_s[1024], sel_s[16];
+    __shared__ uint32_t s_bits[33];
+    __shared__ float red[4];
+    __shared__ int s_last;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int T = a.T;
+    if (a.flags & RS_ROUTER) {
+        const int e = blockIdx.x;
+        // all of this thread's router-row loads first (H <= 8192), then the FMAs
+        constexpr int NI = 8;
+        float4 wv[NI];
+        const float *wr = a.Wr + (size_t)e * a.H;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int k0 = tid * 4 + 1024 * i;
+            wv[i] = (k0 < a.H) ? *reinterpret_cast<const float4 *>(wr + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        if (blockIdx.x == 0 && (a.flags & RS_QUANT))
+            quant_rows_block(a.x, T, a.H, a.xq, a.sa, red);
+        for (int m = 0; m < T; ++m) {
+            uint2 xv[NI];
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int k0 = tid * 4 + 1024 * i;
+                xv[i] = (k0 < a.H) ? *reinterpret_cast<const uint2 *>(a.x + (size_t)m * a.H + k0) : make_uint2(0u, 0u);
+            }
+            double acc = 0.0;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                acc = fma((double)bf16_to_f32(xv[i].x & 0xffffu), (double)wv[i].x, acc);
+                acc = fma((double)bf16_to_f32(xv[i].x >> 16), (double)wv[i].y, acc);
+                acc = fma((double)bf16_to_f32(xv[i].y & 0xffffu), (double)wv[i].z, acc);
+                acc = fma((double)bf16_to_f32(xv[i].y >> 16), (double)wv[i].w, acc);
+            }
+            const double v = wave_sum_d(acc);
+            if (lane == 0)
+                sred[wave][m] = v;
+        }
+        __syncthreads();
+        if (tid < T)
+            store_dev(a.logits + (size_t)tid * a.E + e,
+                      (sred[0][tid] + sred[1][tid]) + (sred[2][tid] + sred[3][tid]));
+        if (!block_arrives_last(a.done, gridDim.x, &s_last))
+            return;
+    }
+    // ---- the last (or only) block ----
+    if ((a.flags & RS_QUANT) && !(a.flags & RS_ROUTER)) {
+        for (int m = 0; m < T; ++m) {
+            const uint16_t *xr = a.x + (size_t)m * a.H;
+            float amax = 0.0f;
+            for (int i = tid * 8; i < a.H; i += 2048) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(xr + i);
+                const uint32_t ww[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    amax = fmaxf(amax, fabsf(bf16_to_f32(ww[j] & 0xffffu)));
+                    amax = fmaxf(amax, fabsf(bf16_to_f32(ww[j] >> 16)));
+                }
+            }
+            amax = block_max_256(amax, red);
+            float inv = 0.0f, sc = 0.0f;
+            if (amax > 0.0f) {
+                inv = 127.0f / amax;
+                sc = amax / 127.0f;
+            }
+            int8_t *qr = a.xq + (size_t)m * a.H;
+            for (int i = tid * 8; i < a.H; i += 2048) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(xr + i);
+                const uint32_t ww[4] = {v.x, v.y, v.z, v.w};
+                uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float xv = bf16_to_f32((j & 1) ? (ww[j >> 1] >> 16) : (ww[j >> 1] & 0xffffu));
+                    const float rr = fminf(fmaxf(rintf(xv * inv), -127.0f), 127.0f);
+                    packed[j >> 2] |= ((uint32_t)(int)rr & 0xffu) << (8 * (j & 3));
+                }
+                *reinterpret_cast<uint2 *>(qr + i) = make_uint2(packed[0], packed[1]);
+            }
+            if (tid == 0)
+                a.sa[m] = sc;
+        }
+    }
+    if (a.flags & RS_ROUTER) {
+        for (int m = 0; m < T; ++m)
+            topk_rank_block(a.logits + (size_t)m * a.E, a.bias, a.E, a.k, a.r,
+                            a.idx + (size_t)m * a.k, a.w + (size_t)m * a.k, s_idx + m * a.k, s_c,
+                            s_s, sel_s);
+        if (tid == 0)
+            *a.done = 0u;
+    } else if (a.flags & RS_LISTS) {
+        for (int j = tid; j < T * a.k; j += 256)
+            s_idx[j] = a.idx[j];
+        __syncthreads();
+    }
+    if (!(a.flags & RS_LISTS))
+        return;
+    const int S = a.k + a.n_shared;
+    const int nE = a.E + a.n_shared;
+    for (int e = tid; e < nE; e += 256)
+        a.cnt[e] = 0;
+    if (tid < 33)
+        s_bits[tid] = 0u;
+    __syncthreads();
+    const int N = T * a.k;
+    for (int j = tid; j < N; j += 256) {
+        const int e = s_idx[j];
+        if (e < 0 || e >= a.E)
+            continue;
+        int pos = 0;
+        bool last = true;
+        for (int jj = 0; jj < N; ++jj) {
+            if (s_idx[jj] == e) {
+                if (jj < j)
+                    ++pos;
+                else if (jj > j)
+                    last = false;
+            }
+        }
+        if (pos < a.list_stride)
+            a.list[(size_t)e * a.list_stride + pos] = (j / a.k) * S + (j % a.k);
+        if (last)
+            a.cnt[e] = pos + 1 < a.list_stride ? pos + 1 : a.list_stride;
+        atomicOr(&s_bits[e >> 5], 1u << (e & 31));
+    }
+    if (a.n_shared) {
+        for (int m = tid; m < T; m += 256)
+            a.list[(size_t)a.E * a.list_stride + m] = m * S + a.k;
+        if (tid == 0) {
+            a.cnt[a.E] = T;
+            atomicOr(&s_bits[a.E >> 5], 1u << (a.E & 31));
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const uint32_t bits = lane < 33 ? s_bits[lane] : 0u;
+        const int nb = __popc(bits);
+        int pre = nb;                            // inclusive prefix over lanes
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(pre, o, 64);
+            if (lane >= o)
+                pre += v;
+        }
+        int pos = pre - nb;
+        for (int b = 0; b < 32; ++b)
+            if ((bits >> b) & 1u)
+                a.active[pos++] = lane * 32 + b;
+        if (lane == 63)
+            *a.n_active = pre;
+    }
+}
+
+hipError_t launch_route_small(const RouteSmallArgs &a, hipStream_t st)
+{
+    const int grid = (a.flags & RS_ROUTER) ? a.E : 1;
+    route_small_kernel<<<grid, 256, 0, st>>>(a);
     return hipGetLastError();
 }
 

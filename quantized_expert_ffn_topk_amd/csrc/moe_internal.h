@@ -83,6 +83,10 @@ struct ProjArgs {
     // activation rows (int8 codes, fp32 scale)
     const int8_t *q;
     const float *s;
+    // few-token down projection: stage rows by requantising these fp32 rows
+    // (SwiGLU outputs) instead of reading q/s; block column 0 also stores the
+    // codes and scales to q/s
+    const float *hsrc;
     int in_by_token;           // 1: input row = slot / S, 0: input row = slot
     int K;
     int group_shift;           // log2(group / 32)
@@ -92,6 +96,42 @@ struct ProjArgs {
     // output rows: out[slot * ldo + 32*pair + 16*j + r]
     float *out;
     int ldo;
+};
+
+// Fused tails of the few-token GEMV path: requantisation of the SwiGLU rows
+// (gate/up) and the combine (down); ctr is a zeroed device counter array.
+struct TailArgs {
+    int8_t *qh;
+    float *sh;
+    int F;
+    const int32_t *idx;
+    const float *w;
+    int T, k, E, n_shared, H, out_dtype;
+    void *out;
+    uint32_t *ctr;
+};
+
+// Few-token routing in one launch (kernels_router.hip).
+enum { RS_ROUTER = 1, RS_QUANT = 2, RS_LISTS = 4 };
+constexpr int RS_MAXT = 16;
+
+struct RouteSmallArgs {
+    const uint16_t *x;
+    int T, H;
+    const float *Wr, *bias;
+    int E, k;
+    float r;
+    double *logits;
+    int32_t *idx;
+    float *w;
+    int flags;
+    int8_t *xq;
+    float *sa;
+    int32_t *cnt, *list;
+    int list_stride;
+    int32_t *active, *n_active;
+    int n_shared;
+    uint32_t *done;
 };
 
 // ---------------------------------------------------------------------------
@@ -107,9 +147,10 @@ hipError_t launch_permute(const int32_t *idx, int T, int k, int E, int n_shared,
                           int32_t *cnt, int32_t *list, int list_stride, int32_t *active,
                           int32_t *n_active, uint32_t *done_counter, hipStream_t st);
 hipError_t launch_gateup_gemv(const ProjArgs &a, int max_active, int F, int mg,
-                              float *h, int ldh, hipStream_t st);
+                              float *h, int ldh, const TailArgs *tail, hipStream_t st);
 hipError_t launch_proj_gemv(const ProjArgs &a, int max_active, int n_pairs, int mg,
-                            hipStream_t st);
+                            const TailArgs *tail, hipStream_t st);
+hipError_t launch_route_small(const RouteSmallArgs &a, hipStream_t st);
 hipError_t launch_requant(const float *h, int rows, int F, int8_t *q, float *s,
                           hipStream_t st);
 hipError_t launch_combine(const float *Y, const int32_t *idx, const float *w, int T,
