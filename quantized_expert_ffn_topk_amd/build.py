@@ -18,7 +18,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-HIP_SOURCES = ["kernels_router.hip", "kernels_gemv.hip", "kernels_gemm.hip", "kernels_mx.hip"]
+HIP_SOURCES = ["kernels_router.hip", "kernels_gemv.hip", "kernels_bs1.hip", "kernels_gemm.hip",
+               "kernels_mx.hip"]
 CPP_SOURCES = ["api.cpp", "pack.cpp", "cache.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math", "-Wall",

@@ -175,6 +175,8 @@ extern "C" moe_status moe_ctx_create(int32_t device, const moe_layer_desc *desc,
     ALLOC(c->qh, T * S * F);
     ALLOC(c->sh, T * S);
     ALLOC(c->Y, T * S * H);
+    ALLOC(c->sel, k);
+    ALLOC(c->cs, 2 * E);
     ALLOC(c->ident, T);
     ALLOC(c->zero1, 1);
     ALLOC(c->one1, 1);
@@ -240,18 +242,32 @@ static moe_status check_call(moe_ctx *ctx, const void *x, int32_t T, const moe_l
 // kernel timing
 // ---------------------------------------------------------------------------
 namespace moe {
+ProfSlot &prof_slot()
+{
+    static thread_local ProfSlot slot;
+    return slot;
+}
+
 void prof_begin(moe_ctx *c, int k, hipStream_t st)
 {
-    if (c->prof_on)
-        (void)hipEventRecord(c->prof_ev[2 * k], st);
+    if (!c->prof_on)
+        return;
+    (void)hipEventRecord(c->prof_ev[2 * k], st);
+    ProfSlot &p = prof_slot();
+    p.start = c->prof_ev[2 * k];
+    p.stop = c->prof_ev[2 * k + 1];
+    p.used = false;
 }
 
 void prof_end(moe_ctx *c, int k, hipStream_t st)
 {
-    if (c->prof_on) {
+    if (!c->prof_on)
+        return;
+    ProfSlot &p = prof_slot();
+    if (!p.used)                 // the launcher did not time the kernel itself
         (void)hipEventRecord(c->prof_ev[2 * k + 1], st);
-        c->prof_used[k] = true;
-    }
+    p = ProfSlot{};
+    c->prof_used[k] = true;
 }
 
 moe_status prof_collect(moe_ctx *c)
@@ -323,6 +339,49 @@ static bool small_path(const moe_ctx *c, int T)
            c->d.hidden <= 8192 && !use_mfma(c, T);
 }
 
+// One token: expert FFN straight from the top-k output (kernels_bs1.hip).
+static bool bs1_path(const moe_ctx *c, int T)
+{
+    return T == 1 && small_path(c, T) &&
+           bs1_supported(c->d.hidden, c->d.ffn, c->d.top_k, c->d.n_shared);
+}
+
+static Bs1Args make_bs1(const moe_ctx *c, const moe_layer_weights *w,
+                        const void *const *expert_ptrs, const int32_t *idx, const float *gw,
+                        void *out, bool sel_ready)
+{
+    const moe_layer_desc &d = c->d;
+    Bs1Args b{};
+    b.ex.ptrs = expert_ptrs;
+    b.ex.shared = w->shared;
+    b.ex.E = d.n_experts;
+    b.sel = sel_ready ? c->sel : nullptr;
+    b.idx = idx;
+    b.w = gw;
+    b.k = d.top_k;
+    b.n_shared = d.n_shared;
+    b.xq = c->xq;
+    b.sa = c->sa;
+    b.H = d.hidden;
+    b.F = d.ffn;
+    b.group_shift = (d.group == 64) ? 1 : 0;
+    b.gu_w = c->L.gu_w;
+    b.gu_s = c->L.gu_s;
+    b.gu_tile_w = c->L.gu_tile_w;
+    b.gu_tile_s = c->L.gu_tile_s;
+    b.dn_w = c->L.dn_w;
+    b.dn_s = c->L.dn_s;
+    b.dn_tile_w = c->L.dn_tile_w;
+    b.dn_tile_s = c->L.dn_tile_s;
+    b.h = c->h;
+    b.qh = c->qh;
+    b.sh = c->sh;
+    b.Y = c->Y;
+    b.out = out;
+    b.out_dtype = d.out_dtype;
+    return b;
+}
+
 static RouteSmallArgs route_small_args(moe_ctx *c, const void *x, int T, const moe_layer_weights *w,
                                        int32_t *idx, float *gw, int flags)
 {
@@ -349,6 +408,8 @@ static RouteSmallArgs route_small_args(moe_ctx *c, const void *x, int T, const m
     r.n_active = c->n_active;
     r.n_shared = d.n_shared;
     r.done = c->done;
+    r.ptrs = w ? w->expert_ptrs : nullptr;
+    r.sel = c->sel;
     return r;
 }
 
@@ -371,6 +432,24 @@ static moe_status router_enqueue(moe_ctx *c, const void *x, int32_t T, const moe
     LAUNCH(MOE_PROF_TOPK, "top-k launch",
            launch_topk(c->logits, w->router_bias, T, d.n_experts, d.top_k, d.routed_scale, idx,
                        gw, st));
+    return MOE_OK;
+}
+
+// One token, E <= 256: router logits, scores and the token codes in one
+// launch, then the top-k (with the shared expert's gate/up beside it).
+static moe_status router_bs1_enqueue(moe_ctx *c, const void *x, const moe_layer_weights *w,
+                                     int32_t *idx, float *gw, bool sel, hipStream_t st)
+{
+    if (!w->router_w || !w->router_bias)
+        return fail(MOE_E_INVAL, "router weights are NULL");
+    if (c->d.n_shared && !w->shared)
+        return fail(MOE_E_INVAL, "shared expert blob is NULL");
+    const RouteSmallArgs ra = route_small_args(c, x, 1, w, idx, gw, RS_QUANT);
+    LAUNCH(MOE_PROF_ROUTER, "router launch", launch_router_bs1(ra, c->cs, st));
+    const Bs1Args b = make_bs1(c, w, nullptr, idx, gw, nullptr, false);
+    LAUNCH(MOE_PROF_TOPK, "top-k launch",
+           launch_topk_bs1(c->cs, c->d.n_experts, c->d.routed_scale, sel ? w->expert_ptrs : nullptr,
+                           idx, gw, c->sel, b, st));
     return MOE_OK;
 }
 
@@ -400,9 +479,13 @@ static int mg_for(int T)
     return mg;
 }
 
+// prepped: the router launch already quantised x (and built the lists, or
+// with sel_ready selected the blobs of the ranks; with shared_done it also ran
+// the shared expert's gate/up).
 static moe_status ffn_enqueue(moe_ctx *c, const void *x, int32_t T, const moe_layer_weights *w,
                               const void *const *expert_ptrs, const int32_t *idx,
-                              const float *gw, void *out, hipStream_t st, bool prepped = false)
+                              const float *gw, void *out, hipStream_t st, bool prepped = false,
+                              bool sel_ready = false, bool shared_done = false)
 {
     const moe_layer_desc &d = c->d;
     const int H = d.hidden, F = d.ffn, E = d.n_experts, k = d.top_k;
@@ -412,6 +495,20 @@ static moe_status ffn_enqueue(moe_ctx *c, const void *x, int32_t T, const moe_la
         return fail(MOE_E_INVAL, "expert_ptrs is NULL");
     if (d.wfmt == MOE_WFMT_MXFP4)
         return mx_ffn_enqueue(c, x, T, w, expert_ptrs, idx, gw, out, st);
+    if (bs1_path(c, T)) {
+        if (!prepped) {
+            RouteSmallArgs ra = route_small_args(c, x, T, nullptr, const_cast<int32_t *>(idx),
+                                                 const_cast<float *>(gw), RS_QUANT | RS_SEL);
+            ra.ptrs = expert_ptrs;
+            LAUNCH(MOE_PROF_QUANT, "quant launch", launch_route_small(ra, st));
+            sel_ready = true;
+        }
+        const Bs1Args b = make_bs1(c, w, expert_ptrs, idx, gw, out, sel_ready);
+        LAUNCH(MOE_PROF_GATEUP, "gate/up launch",
+               launch_gateup_bs1(b, shared_done ? k : k + d.n_shared, st));
+        LAUNCH(MOE_PROF_DOWN, "down launch", launch_down_bs1(b, st));
+        return MOE_OK;
+    }
     const bool small = small_path(c, T);
     if (small && !prepped) {
         LAUNCH(MOE_PROF_QUANT, "quant/lists launch",
@@ -536,22 +633,30 @@ extern "C" moe_status moe_layer_forward(moe_ctx *ctx, const void *x, int32_t T,
     int32_t *idx = idx_out ? idx_out : ctx->idx;
     float *gw = gate_w_out ? gate_w_out : ctx->gw;
     ctx->last_T = T;
+    // few tokens: quantisation (and the routing lists, unless one token needs
+    // none) ride on the router launch.  One token with E <= 256: the router is
+    // two launches, the second also runs the shared expert's gate/up and,
+    // without the cache, picks the ranks' blobs.
     const bool fused = small_path(ctx, T) && ctx->d.wfmt == MOE_WFMT_INT4;
-    s = router_enqueue(ctx, x, T, w, idx, gw, st, fused ? (RS_QUANT | RS_LISTS) : 0);
+    const bool bs1 = bs1_path(ctx, T);
+    const bool two = bs1 && ctx->d.n_experts <= 256;
+    const bool sel = two && !cache && w->expert_ptrs;
+    if (two)
+        s = router_bs1_enqueue(ctx, x, w, idx, gw, sel, st);
+    else
+        s = router_enqueue(ctx, x, T, w, idx, gw, st,
+                           bs1 ? RS_QUANT : fused ? (RS_QUANT | RS_LISTS) : 0);
     if (s)
         return s;
-    if (!cache) {
-        s = ffn_enqueue(ctx, x, T, w, w->expert_ptrs, idx, gw, out, st, fused);
+    const void *const *ptrs = w->expert_ptrs;
+    if (cache) {
+        // the caller may prefetch the next layer after this call, then calls
+        // moe_cache_release
+        s = cache_demand_for_layer(cache, ctx->d, layer, idx, T, st, &ptrs);
         if (s)
             return s;
-        return prof_collect(ctx);
     }
-    const void *const *table = nullptr;
-    s = cache_demand_for_layer(cache, ctx->d, layer, idx, T, st, &table);
-    if (s)
-        return s;
-    // the caller may prefetch the next layer now, then calls moe_cache_release
-    s = ffn_enqueue(ctx, x, T, w, table, idx, gw, out, st, fused);
+    s = ffn_enqueue(ctx, x, T, w, ptrs, idx, gw, out, st, fused, sel, two && ctx->d.n_shared);
     if (s)
         return s;
     return prof_collect(ctx);

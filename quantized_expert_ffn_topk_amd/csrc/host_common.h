@@ -32,6 +32,8 @@ struct moe_ctx {
     int8_t *qh = nullptr;
     float *sh = nullptr;
     float *Y = nullptr;
+    const void **sel = nullptr;   // one-token path: blob of each rank
+    double *cs = nullptr;         // one-token path: biased scores and scores [2E]
     // MFMA path: tile work list
     int32_t *tiles = nullptr, *n_tiles = nullptr;
     int max_tiles = 0;

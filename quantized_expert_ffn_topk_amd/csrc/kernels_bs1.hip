@@ -1,0 +1,431 @@
+// kernels_bs1.hip -- expert FFN for one token (batch-1 decode) on gfx950.
+//
+// With one token every routed expert and the shared expert has exactly one
+// row, so slot i is rank i (i = top_k: shared expert) and the kernels read
+// the expert of a slot straight from the top-k output: no routing lists.
+//
+// Both kernels stream the expert weights once.  A wave owns a 16-row tile of
+// an expert (blob layout [tile][kc][r][16 B]); lane l owns row l&15 and the
+// chunks kc = 4j + (l>>4), so the 64 lanes of one 16-byte load read 1 KiB of
+// contiguous blob.  Each int32 group dot (v_dot4_i32_i8 on nibbles masked
+// into the top of their bytes, see kernels_gemv.hip) is scaled in fp64 and
+// summed; those sums are exact, so the split over lanes does not change the
+// result.  Integer-dot scheme: Colibri guide, table "Points techniques cles".
+//
+//   gateup_bs1_kernel : block (slot, b) = 2 waves, the gate tile 2b and the up
+//                       tile 2b+1 over all of K = hidden; SwiGLU of the 16 rows.
+//   down_bs1_kernel   : block = 32 output rows, one wave per slot.  Each wave
+//                       requantises its slot's SwiGLU row (same rule as the
+//                       token quantisation) into LDS, projects both 16-row
+//                       tiles, and the block then combines
+//                       the slots of the 32 outputs: shared expert first, then
+//                       rank order, in fp64, rounded once.  No cross-block
+//                       hand-off inside a kernel.
+#include "device_common.h"
+#include "host_common.h"
+#include "topk_common.h"
+
+namespace moe {
+
+// One batch of U 16-byte weight loads and their fp16 scales.
+template <int U>
+__device__ __forceinline__ void bs1_load(const uint4 *__restrict__ wp,
+                                         const uint16_t *__restrict__ sp, int sstride, int j0,
+                                         uint4 (&wv)[U], uint16_t (&sv)[U])
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        wv[u] = wp[(size_t)64 * (j0 + u)];
+        sv[u] = sp[(size_t)sstride * (j0 + u)];
+    }
+}
+
+// Adds the exact group sums of one batch: chunk kc = 4(j0+u) + c4 of the
+// lane's row against the activation codes in LDS.
+template <int U>
+__device__ __forceinline__ double bs1_dot(const uint4 (&wv)[U], const uint16_t (&sv)[U], int j0,
+                                          int c4, const int8_t *__restrict__ lq, double p)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = 4 * (j0 + u) + c4;
+        const int4 *qa = reinterpret_cast<const int4 *>(lq + c * 32);
+        const int4 a0 = qa[0], a1 = qa[1];
+        const uint32_t wd[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+        int acc = 0;
+        acc = sdot4((int)((wd[0] << 4) & 0xf0f0f0f0u), a0.x, acc);
+        acc = sdot4((int)((wd[1] << 4) & 0xf0f0f0f0u), a0.y, acc);
+        acc = sdot4((int)((wd[2] << 4) & 0xf0f0f0f0u), a0.z, acc);
+        acc = sdot4((int)((wd[3] << 4) & 0xf0f0f0f0u), a0.w, acc);
+        acc = sdot4((int)(wd[0] & 0xf0f0f0f0u), a1.x, acc);
+        acc = sdot4((int)(wd[1] & 0xf0f0f0f0u), a1.y, acc);
+        acc = sdot4((int)(wd[2] & 0xf0f0f0f0u), a1.z, acc);
+        acc = sdot4((int)(wd[3] & 0xf0f0f0f0u), a1.w, acc);
+        // 16 x the group dot; S/16 is exact
+        p = fma((double)acc, (double)f16_to_f32(sv[u]) * 0.0625, p);
+    }
+    return p;
+}
+
+// Blob of slot ai, or NULL when the slot's expert id is out of range (such a
+// slot contributes nothing, as in the combine).  With the router's blob
+// selection this is one load; otherwise the id, then the pointer table.
+__device__ __forceinline__ const uint8_t *bs1_slot_blob(const Bs1Args &a, int ai)
+{
+    if (ai >= a.k)
+        return reinterpret_cast<const uint8_t *>(a.ex.shared);
+    if (a.sel)
+        return reinterpret_cast<const uint8_t *>(a.sel[ai]);
+    const int e = a.idx[ai];
+    return (e >= 0 && e < a.ex.E) ? reinterpret_cast<const uint8_t *>(a.ex.ptrs[e]) : nullptr;
+}
+
+// ---------------------------------------------------------------------------
+// Gate/up + SwiGLU: h[slot, 16b + r] = fp32(G/(1+exp(-G)) * U) with
+// G, U = exact sum * token scale (fp64).
+// ---------------------------------------------------------------------------
+// NP tile pairs per block of 128*NP*KS threads: pair p = b0 + p' has its gate
+// tile 2b and up tile 2b+1, each split over KS waves by K (wave w: pair w /
+// (2 KS), tile half (w / KS) % 2, K segment w % KS).  The KS partial sums of a
+// row are exact, so adding them in any order gives the exact sum.
+template <int U, int NP, int KS>
+__device__ __forceinline__ void gateup_pairs(const Bs1Args &a, int ai, int b0, unsigned char *smem)
+{
+    constexpr int NT = 128 * NP * KS;
+    constexpr int XS = (512 + NT - 1) / NT;          // H <= 8192: 512 x 16 B of codes
+    __shared__ double sp[NP][2][KS][16];
+    // the token codes are fetched while the blob pointer is looked up
+    const uint4 *xsrc = reinterpret_cast<const uint4 *>(a.xq);
+    const int nx = a.H >> 4;
+    uint4 xs[XS];
+#pragma unroll
+    for (int i = 0; i < XS; ++i)                     // clamped: every load in bounds
+        xs[i] = xsrc[min((int)threadIdx.x + NT * i, nx - 1)];
+    const uint8_t *blob = bs1_slot_blob(a, ai);
+    if (!blob)
+        return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int seg = wave % KS, half = (wave / KS) & 1, pair = wave / (2 * KS), b = b0 + pair;
+    const int r = lane & 15, c4 = lane >> 4, gs = a.group_shift;
+    const int tile = 2 * b + half;
+    const uint4 *wp = reinterpret_cast<const uint4 *>(blob + a.gu_w + (size_t)tile * a.gu_tile_w) + lane;
+    const uint16_t *sp_ = reinterpret_cast<const uint16_t *>(blob + a.gu_s + (size_t)tile * a.gu_tile_s) +
+                          (((c4 >> gs) << 4) + r);
+    const int sstride = 64 >> gs;
+    const int nseg = (a.H >> 7) / KS, j_begin = seg * nseg, j_end = j_begin + nseg;
+
+    uint4 wv[U];
+    uint16_t sv[U];
+    bs1_load<U>(wp, sp_, sstride, j_begin, wv, sv);
+    {
+        uint4 *dst = reinterpret_cast<uint4 *>(smem);
+#pragma unroll
+        for (int i = 0; i < XS; ++i)
+            if ((int)threadIdx.x + NT * i < nx)
+                dst[threadIdx.x + NT * i] = xs[i];
+    }
+    __syncthreads();
+    const int8_t *lq = reinterpret_cast<const int8_t *>(smem);
+    double p = bs1_dot<U>(wv, sv, j_begin, c4, lq, 0.0);
+    for (int j0 = j_begin + U; j0 < j_end; j0 += U) {
+        bs1_load<U>(wp, sp_, sstride, j0, wv, sv);
+        p = bs1_dot<U>(wv, sv, j0, c4, lq, p);
+    }
+    p += shfl_xor_d(p, 16);
+    p += shfl_xor_d(p, 32);
+    if (lane < 16)
+        sp[pair][half][seg][lane] = p;
+    __syncthreads();
+    if (half == 0 && seg == 0 && lane < 16) {
+        double g = 0.0, u = 0.0;
+#pragma unroll
+        for (int q = 0; q < KS; ++q) {
+            g += sp[pair][0][q][lane];
+            u += sp[pair][1][q][lane];
+        }
+        const double sa = (double)a.sa[0];
+        const double G = g * sa;
+        const double Uv = u * sa;
+        const double silu = G / (1.0 + exp(-G));
+        a.h[(size_t)ai * a.F + 16 * b + lane] = (float)(silu * Uv);
+    }
+}
+
+// Block (slot, b): the tile pair b of the slot's expert, K split over KS waves.
+template <int U, int KS>
+__global__ __launch_bounds__(128 * KS) void gateup_bs1_kernel(Bs1Args a)
+{
+    extern __shared__ __align__(16) unsigned char smem[];   // H activation codes
+    gateup_pairs<U, 1, KS>(a, blockIdx.x, blockIdx.y, smem);
+}
+
+// ---------------------------------------------------------------------------
+// Second launch of the one-token router (after router_bs1_kernel): block 0
+// selects the top k from the biased scores c and scores s (cs = [c | s]),
+// writes ids, weights and the ranks' blobs.  The other blocks run the shared
+// expert's gate/up meanwhile (it needs no routing): block 1 + q takes the tile
+// pair q with K split over 2 waves per tile, so the routed gate/up launch that
+// follows is k slots wide.
+// ---------------------------------------------------------------------------
+template <int U>
+__global__ __launch_bounds__(256) void topk_bs1_kernel(const double *__restrict__ cs, int E,
+                                                       float r, const void *const *ptrs,
+                                                       int32_t *idx_out, float *w_out,
+                                                       const void **sel, Bs1Args a)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    if (blockIdx.x > 0) {
+        gateup_pairs<U, 1, 2>(a, a.k, blockIdx.x - 1, smem);
+        return;
+    }
+    __shared__ double s_s[256], cand_c[64], sel_s[16];
+    __shared__ int cand_i[64], s_idx[16];
+    __shared__ const void *s_ptr[256];
+    const int tid = threadIdx.x;
+    double c = -INFINITY;
+    int ci = INT_MAX;
+    if (tid < E) {
+        c = cs[tid];
+        s_s[tid] = cs[E + tid];
+        ci = tid;
+        if (ptrs)
+            s_ptr[tid] = ptrs[tid];
+    }
+    topk_select_256(c, ci, s_s, a.k, r, idx_out, w_out, s_idx, cand_c, cand_i, sel_s);
+    if (ptrs && tid < a.k)
+        sel[tid] = s_ptr[s_idx[tid]];
+}
+
+// ---------------------------------------------------------------------------
+// Down projection + combine for output rows [32p, 32p + 32): the two 16-row
+// tiles 2p, 2p+1 of every slot.  F <= 2048.  Each wave codes its slot's
+// SwiGLU row with the token quantisation rule (amax over the row, inv =
+// 127/amax, s = amax/127, q = rint(h*inv) clamped to [-127, 127]) into LDS,
+// then streams both tiles with two batches of U loads in flight.
+// ---------------------------------------------------------------------------
+template <int U>
+__device__ __forceinline__ void bs1_load2(const uint4 *wp, const uint16_t *sp, size_t wstep,
+                                          size_t sstep, int sstride, int j, int nj,
+                                          uint4 (&wv)[U], uint16_t (&sv)[U])
+{
+    if (j < nj)
+        bs1_load<U>(wp, sp, sstride, j, wv, sv);
+    else
+        bs1_load<U>(wp + wstep, sp + sstep, sstride, j - nj, wv, sv);
+}
+
+template <int U, int NW, bool DB>
+__global__ __launch_bounds__(64 * NW) void down_bs1_kernel(Bs1Args a)
+{
+    extern __shared__ __align__(16) unsigned char smem[];   // S rows of F codes
+    __shared__ float sY[16][32];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, c4 = lane >> 4, gs = a.group_shift;
+    const int ai = wave, pr = blockIdx.x;
+    const int F = a.F, nj = F >> 7;
+    int8_t *lq = reinterpret_cast<int8_t *>(smem) + (size_t)ai * F;
+
+    uint4 wa[U], wb[U];
+    uint16_t sa[U], sb[U];
+    const uint4 *wp = nullptr;
+    const uint16_t *sp = nullptr;
+    size_t wstep = 0, sstep = 0;
+    const int sstride = 64 >> gs;
+    float sc = 0.0f;
+    // the SwiGLU row first: it depends on nothing and comes from L2, ahead of
+    // the weights in the wave's load queue
+    const float4 *hr = reinterpret_cast<const float4 *>(a.h + (size_t)ai * F);
+    const int nv = F >> 8;                           // float4 per lane, <= 8
+    float4 hv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (i < nv)
+            hv[i] = hr[lane + 64 * i];
+    const uint8_t *blob = bs1_slot_blob(a, ai);
+    if (blob) {
+        wp = reinterpret_cast<const uint4 *>(blob + a.dn_w + (size_t)(2 * pr) * a.dn_tile_w) + lane;
+        sp = reinterpret_cast<const uint16_t *>(blob + a.dn_s + (size_t)(2 * pr) * a.dn_tile_s) +
+             (((c4 >> gs) << 4) + r);
+        wstep = a.dn_tile_w >> 4;
+        sstep = a.dn_tile_s >> 1;
+        bs1_load<U>(wp, sp, sstride, 0, wa, sa);
+        if (DB)
+            bs1_load2<U>(wp, sp, wstep, sstep, sstride, U, nj, wb, sb);
+
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i < nv)
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(hv[i].x), fabsf(hv[i].y)),
+                                         fmaxf(fabsf(hv[i].z), fabsf(hv[i].w))));
+        amax = wave_max(amax);
+        float inv = 0.0f;
+        if (amax > 0.0f) {
+            inv = 127.0f / amax;
+            sc = amax / 127.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i < nv) {
+                const float vv[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w};
+                uint32_t packed = 0u;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float q = fminf(fmaxf(rintf(vv[j] * inv), -127.0f), 127.0f);
+                    packed |= ((uint32_t)(int)q & 0xffu) << (8 * j);
+                }
+                const int o = 4 * (lane + 64 * i);
+                *reinterpret_cast<uint32_t *>(lq + o) = packed;
+                if (pr == 0)
+                    *reinterpret_cast<uint32_t *>(a.qh + (size_t)ai * F + o) = packed;
+            }
+        }
+        if (pr == 0 && lane == 0)
+            a.sh[ai] = sc;
+        // only this wave reads its codes: wait for its LDS writes
+        __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+    }
+    if (blob) {
+        // batches j0 = 0, U, 2U, ... over both tiles (U divides nj, so no batch
+        // straddles them); two in flight: compute one while the next loads
+        const int nb = 2 * nj;
+        double p = 0.0, p0 = 0.0;                  // p: the tile being summed
+        if (DB) {
+            // two batches in flight: compute one while the next loads
+            for (int j0 = 0; j0 < nb; j0 += 2 * U) {
+                if (j0 == nj) {
+                    p0 = p;
+                    p = 0.0;
+                }
+                p = bs1_dot<U>(wa, sa, j0 < nj ? j0 : j0 - nj, c4, lq, p);
+                if (j0 + 2 * U < nb)
+                    bs1_load2<U>(wp, sp, wstep, sstep, sstride, j0 + 2 * U, nj, wa, sa);
+                const int j1 = j0 + U;
+                if (j1 == nj) {
+                    p0 = p;
+                    p = 0.0;
+                }
+                p = bs1_dot<U>(wb, sb, j1 < nj ? j1 : j1 - nj, c4, lq, p);
+                if (j0 + 3 * U < nb)
+                    bs1_load2<U>(wp, sp, wstep, sstep, sstride, j0 + 3 * U, nj, wb, sb);
+            }
+        } else {
+            for (int j0 = 0; j0 < nb; j0 += U) {
+                if (j0 == nj) {
+                    p0 = p;
+                    p = 0.0;
+                }
+                if (j0)
+                    bs1_load2<U>(wp, sp, wstep, sstep, sstride, j0, nj, wa, sa);
+                p = bs1_dot<U>(wa, sa, j0 < nj ? j0 : j0 - nj, c4, lq, p);
+            }
+        }
+        double p1 = p;
+        p0 += shfl_xor_d(p0, 16);
+        p0 += shfl_xor_d(p0, 32);
+        p1 += shfl_xor_d(p1, 16);
+        p1 += shfl_xor_d(p1, 32);
+        if (lane < 16) {
+            const float y0 = (float)(p0 * (double)sc), y1 = (float)(p1 * (double)sc);
+            sY[ai][r] = y0;
+            sY[ai][16 + r] = y1;
+            float *yg = a.Y + (size_t)ai * a.H + 32 * pr;
+            yg[r] = y0;
+            yg[16 + r] = y1;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < 32) {
+        double o = a.n_shared ? (double)sY[a.k][threadIdx.x] : 0.0;
+        for (int i = 0; i < a.k; ++i) {
+            const int ex = a.idx[i];
+            if (ex >= 0 && ex < a.ex.E)
+                o = fma((double)a.w[i], (double)sY[i][threadIdx.x], o);
+        }
+        const float f = (float)o;
+        const size_t n = (size_t)32 * pr + threadIdx.x;
+        if (a.out_dtype == MOE_DT_BF16)
+            reinterpret_cast<uint16_t *>(a.out)[n] = f32_to_bf16(f);
+        else
+            reinterpret_cast<float *>(a.out)[n] = f;
+    }
+}
+
+// Loads per lane per batch: the largest of umax, ..., 4, 2 dividing nj = K/128
+// (K is a multiple of 256, so nj is even).
+static int bs1_u(int nj, int umax)
+{
+    static const int cand[] = {16, 12, 8, 4, 2};
+    for (int u : cand)
+        if (u <= umax && nj % u == 0)
+            return u;
+    return 1;
+}
+
+bool bs1_supported(int H, int F, int k, int n_shared)
+{
+    return F <= 2048 && H <= 8192 && k + n_shared <= 16;
+}
+
+// slots: how many slots from 0 the launch covers (k when the shared expert
+// already ran in the top-k launch, k + n_shared otherwise).
+#ifndef MOE_BS1_GU_KS
+#define MOE_BS1_GU_KS 2
+#endif
+
+template <int KS>
+static void gateup_bs1_u(const Bs1Args &a, dim3 grid, size_t lds, hipStream_t st)
+{
+    switch (bs1_u((a.H >> 7) / KS, 16)) {
+    case 16: launch(gateup_bs1_kernel<16, KS>, grid, 128 * KS, lds, st, a); break;
+    case 12: launch(gateup_bs1_kernel<12, KS>, grid, 128 * KS, lds, st, a); break;
+    case 8: launch(gateup_bs1_kernel<8, KS>, grid, 128 * KS, lds, st, a); break;
+    case 4: launch(gateup_bs1_kernel<4, KS>, grid, 128 * KS, lds, st, a); break;
+    case 2: launch(gateup_bs1_kernel<2, KS>, grid, 128 * KS, lds, st, a); break;
+    default: launch(gateup_bs1_kernel<1, KS>, grid, 128 * KS, lds, st, a); break;
+    }
+}
+
+// slots: how many slots from 0 the launch covers (k when the shared expert
+// already ran in the top-k launch, k + n_shared otherwise).
+hipError_t launch_gateup_bs1(const Bs1Args &a, int slots, hipStream_t st)
+{
+    const dim3 grid(slots, a.F / 16);
+    const size_t lds = (size_t)a.H;
+    gateup_bs1_u<MOE_BS1_GU_KS>(a, grid, lds, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_bs1(const double *cs, int E, float r, const void *const *ptrs,
+                           int32_t *idx_out, float *w_out, const void **sel, const Bs1Args &a,
+                           hipStream_t st)
+{
+    const int blocks = 1 + (a.n_shared ? a.F / 16 : 0);
+    const size_t lds = (size_t)a.H;
+    switch (bs1_u((a.H >> 7) / 2, 16)) {
+    case 16: launch(topk_bs1_kernel<16>, blocks, 256, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); break;
+    case 12: launch(topk_bs1_kernel<12>, blocks, 256, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); break;
+    case 8: launch(topk_bs1_kernel<8>, blocks, 256, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); break;
+    case 4: launch(topk_bs1_kernel<4>, blocks, 256, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); break;
+    case 2: launch(topk_bs1_kernel<2>, blocks, 256, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); break;
+    default: launch(topk_bs1_kernel<1>, blocks, 256, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_down_bs1(const Bs1Args &a, hipStream_t st)
+{
+    const int S = a.k + a.n_shared;
+    const dim3 grid(a.H / 32);
+    const size_t lds = (size_t)S * a.F;
+    // two batches of 2 loads in flight per wave next to the SwiGLU row: for up
+    // to 9 slots the block may use 3 waves per SIMD, for up to 16 slots 4
+    if (S <= 9)
+        launch(down_bs1_kernel<2, 9, true>, grid, 64 * S, lds, st, a);
+    else
+        launch(down_bs1_kernel<2, 16, true>, grid, 64 * S, lds, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(1024) void mfma_tiles_kernel(const int32_t *__restr
 hipError_t launch_mfma_tiles(moe_ctx *c, int T, hipStream_t st)
 {
     (void)T;
-    mfma_tiles_kernel<<<1, 1024, 0, st>>>(c->cnt, c->d.n_experts + c->d.n_shared,
+    launch(mfma_tiles_kernel, 1, 1024, 0, st, c->cnt, c->d.n_experts + c->d.n_shared,
                                           reinterpret_cast<int2 *>(c->tiles), c->n_tiles);
     return hipGetLastError();
 }
@@ -95,7 +95,7 @@ hipError_t launch_mfma_tiles(moe_ctx *c, int T, hipStream_t st)
 hipError_t launch_mfma_tiles_single(moe_ctx *c, int T, hipStream_t st)
 {
     (void)T;
-    mfma_tiles_kernel<<<1, 1024, 0, st>>>(c->dbg_cnt, 1, reinterpret_cast<int2 *>(c->tiles),
+    launch(mfma_tiles_kernel, 1, 1024, 0, st, c->dbg_cnt, 1, reinterpret_cast<int2 *>(c->tiles),
                                           c->n_tiles);
     return hipGetLastError();
 }
@@ -369,9 +369,9 @@ hipError_t launch_gateup_mfma(const ProjArgs &a, const moe_ctx *c, int T, int F,
     const int grid = grid_for(mt_max, F / 64);
     const int2 *tl = reinterpret_cast<const int2 *>(c->tiles);
     if (a.group_shift)
-        mfma_proj_kernel<true, 2><<<grid, 512, 0, st>>>(a, tl, c->n_tiles, mt_max, F / 64, h, ldh);
+        launch(mfma_proj_kernel<true, 2>, grid, 512, 0, st, a, tl, c->n_tiles, mt_max, F / 64, h, ldh);
     else
-        mfma_proj_kernel<true, 1><<<grid, 512, 0, st>>>(a, tl, c->n_tiles, mt_max, F / 64, h, ldh);
+        launch(mfma_proj_kernel<true, 1>, grid, 512, 0, st, a, tl, c->n_tiles, mt_max, F / 64, h, ldh);
     return hipGetLastError();
 }
 
@@ -382,9 +382,9 @@ hipError_t launch_proj_mfma(const ProjArgs &a, const moe_ctx *c, int T, int n_ro
     const int grid = grid_for(mt_max, n_rows / 128);
     const int2 *tl = reinterpret_cast<const int2 *>(c->tiles);
     if (a.group_shift)
-        mfma_proj_kernel<false, 2><<<grid, 512, 0, st>>>(a, tl, c->n_tiles, mt_max, n_rows / 128, a.out, a.ldo);
+        launch(mfma_proj_kernel<false, 2>, grid, 512, 0, st, a, tl, c->n_tiles, mt_max, n_rows / 128, a.out, a.ldo);
     else
-        mfma_proj_kernel<false, 1><<<grid, 512, 0, st>>>(a, tl, c->n_tiles, mt_max, n_rows / 128, a.out, a.ldo);
+        launch(mfma_proj_kernel<false, 1>, grid, 512, 0, st, a, tl, c->n_tiles, mt_max, n_rows / 128, a.out, a.ldo);
     return hipGetLastError();
 }
 

@@ -435,7 +435,7 @@ static void launch_gateup_u(const ProjArgs &a, dim3 grid, size_t lds, float *h, 
     // 12 loads of 16 B per lane per batch measured best on the GLM-shaped
     // decode layer (24: fewer, larger batches oversubscribe HBM; 8: too few)
     (void)niter;
-    gateup_gemv_kernel<MG, 12, TAIL><<<grid, 256, lds, st>>>(a, h, ldh, t);
+    launch(gateup_gemv_kernel<MG, 12, TAIL>, grid, 256, lds, st, a, h, ldh, t);
 }
 
 template <int MG, bool TAIL>
@@ -443,7 +443,7 @@ static void launch_proj_u(const ProjArgs &a, dim3 grid, size_t lds, const TailAr
                           hipStream_t st)
 {
     (void)niter;
-    proj_gemv_kernel<MG, 12, TAIL><<<grid, 256, lds, st>>>(a, t);
+    launch(proj_gemv_kernel<MG, 12, TAIL>, grid, 256, lds, st, a, t);
 }
 
 hipError_t launch_gateup_gemv(const ProjArgs &a, int max_active, int F, int mg, float *h, int ldh,
@@ -506,7 +506,7 @@ hipError_t launch_requant(const float *h, int rows, int F, int8_t *q, float *s, 
 {
     if (rows <= 0)
         return hipSuccess;
-    requant_kernel<<<rows, 256, 0, st>>>(h, F, q, s);
+    launch(requant_kernel, rows, 256, 0, st, h, F, q, s);
     return hipGetLastError();
 }
 
@@ -545,7 +545,7 @@ hipError_t launch_combine(const float *Y, const int32_t *idx, const float *w, in
     if (T <= 0)
         return hipSuccess;
     dim3 grid((H + 255) / 256, T);
-    combine_kernel<<<grid, 256, 0, st>>>(Y, idx, w, k, E, n_shared, H, out, out_dtype);
+    launch(combine_kernel, grid, 256, 0, st, Y, idx, w, k, E, n_shared, H, out, out_dtype);
     return hipGetLastError();
 }
 

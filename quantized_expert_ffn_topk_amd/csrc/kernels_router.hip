@@ -8,6 +8,7 @@
 // computed in fp64 so that the choice does not depend on summation order.
 #include "device_common.h"
 #include "moe_internal.h"
+#include "topk_common.h"
 
 #include <climits>
 
@@ -65,7 +66,7 @@ hipError_t launch_quant_tokens(const uint16_t *x, int T, int H, int8_t *q, float
 {
     if (T <= 0)
         return hipSuccess;
-    quant_tokens_kernel<<<T, 256, 0, st>>>(x, H, q, s);
+    launch(quant_tokens_kernel, T, 256, 0, st, x, H, q, s);
     return hipGetLastError();
 }
 
@@ -172,10 +173,10 @@ hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *Wr
         return hipSuccess;
     if (T <= 16) {
         dim3 grid((E + 3) / 4, (T + 3) / 4);
-        router_gemv_kernel<4><<<grid, 256, 0, st>>>(x, T, H, Wr, E, logits);
+        launch(router_gemv_kernel<4>, grid, 256, 0, st, x, T, H, Wr, E, logits);
     } else {
         dim3 grid((E + 63) / 64, (T + 63) / 64);
-        router_gemm_kernel<<<grid, 256, 0, st>>>(x, T, H, Wr, E, logits);
+        launch(router_gemm_kernel, grid, 256, 0, st, x, T, H, Wr, E, logits);
     }
     return hipGetLastError();
 }
@@ -259,7 +260,7 @@ hipError_t launch_topk(const double *logits, const float *bias, int T, int E, in
 {
     if (T <= 0)
         return hipSuccess;
-    topk_kernel<<<(T + 3) / 4, 256, 0, st>>>(logits, bias, T, E, k, r, idx, w);
+    launch(topk_kernel, (T + 3) / 4, 256, 0, st, logits, bias, T, E, k, r, idx, w);
     return hipGetLastError();
 }
 
@@ -336,7 +337,7 @@ hipError_t launch_permute(const int32_t *idx, int T, int k, int E, int n_shared,
                           int32_t *list, int list_stride, int32_t *active, int32_t *n_active,
                           uint32_t *done_counter, hipStream_t st)
 {
-    permute_kernel<<<E + n_shared, 256, 0, st>>>(idx, T, k, E, n_shared, cnt, list, list_stride,
+    launch(permute_kernel, E + n_shared, 256, 0, st, idx, T, k, E, n_shared, cnt, list, list_stride,
                                                   active, n_active, done_counter);
     return hipGetLastError();
 }
@@ -355,7 +356,7 @@ __global__ void set_i32_kernel(int32_t *p, int32_t v)
 
 hipError_t launch_set_i32(int32_t *p, int32_t v, hipStream_t st)
 {
-    set_i32_kernel<<<1, 1, 0, st>>>(p, v);
+    launch(set_i32_kernel, 1, 1, 0, st, p, v);
     return hipGetLastError();
 }
 
@@ -370,7 +371,7 @@ __global__ void table_update_kernel(const void **table, int set_idx, const void 
 hipError_t launch_table_update(const void **table, int set_idx, const void *ptr, int clear_idx,
                                hipStream_t st)
 {
-    table_update_kernel<<<1, 1, 0, st>>>(table, set_idx, ptr, clear_idx);
+    launch(table_update_kernel, 1, 1, 0, st, table, set_idx, ptr, clear_idx);
     return hipGetLastError();
 }
 
@@ -382,10 +383,12 @@ namespace moe {
 // Few-token routing in one launch (decode).  With RS_ROUTER, block e computes
 // the fp64 logits of expert e for all T tokens (each thread a fixed slice of
 // H, then a fixed-order block reduction); the last block to finish then runs
-// the per-token top-k.  The same last block (or the single block when the
-// router is not part of the call) quantises the tokens and builds the routing
-// lists: per expert its slots in token order, the shared expert's slots, and
-// the list of experts with rows.
+// the per-token top-k.  Every block has read all of x, so with RS_QUANT the
+// blocks also share the token quantisation (each codes a slice once the block
+// is past the hand-off); without the router a single block quantises.  The
+// last (or single) block then builds the routing lists (RS_LISTS): per expert
+// its slots in token order, the shared expert's slots, and the list of experts
+// with rows.
 // ---------------------------------------------------------------------------
 // Top-k of one token by ranks: every thread takes experts e = tid + 256j and
 // counts the experts that precede e in the order (c desc, index asc); experts
@@ -431,59 +434,80 @@ __device__ __forceinline__ void topk_rank_block(const double *__restrict__ lg,
     __syncthreads();
 }
 
-// Per-token int8 quantisation of T rows by one block (same rule as
-// quant_tokens_kernel).
-__device__ __noinline__ void quant_rows_block(const uint16_t *__restrict__ x, int T, int H,
-                                              int8_t *__restrict__ xq, float *__restrict__ sa,
-                                              float *red)
+// Top-k of one token for E <= 256 from the fp64 logits written by the other
+// blocks (load_dev): sigmoid scores, biased scores, then topk_select_256.
+__device__ __forceinline__ void topk_sort_block(const double *__restrict__ lg,
+                                                const float *__restrict__ bias, int E, int k,
+                                                float r, int32_t *__restrict__ idx_out,
+                                                float *__restrict__ w_out, int32_t *s_idx,
+                                                double *s_s, double *cand_c, int *cand_i,
+                                                double *sel_s)
 {
     const int tid = threadIdx.x;
-    for (int m = 0; m < T; ++m) {
-        const uint16_t *xr = x + (size_t)m * H;
-        float amax = 0.0f;
-        for (int i = tid * 8; i < H; i += 2048) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(xr + i);
-            const uint32_t ww[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                amax = fmaxf(amax, fabsf(bf16_to_f32(ww[j] & 0xffffu)));
-                amax = fmaxf(amax, fabsf(bf16_to_f32(ww[j] >> 16)));
-            }
-        }
-        amax = block_max_256(amax, red);
+    double c = -INFINITY;
+    int ci = INT_MAX;
+    if (tid < E) {
+        const double sv = 1.0 / (1.0 + exp(-load_dev(lg + tid)));
+        const double cv = sv + (double)bias[tid];
+        s_s[tid] = sv;
+        c = (cv != cv) ? -INFINITY : cv;
+        ci = tid;
+    }
+    topk_select_256(c, ci, s_s, k, r, idx_out, w_out, s_idx, cand_c, cand_i, sel_s);
+}
+
+// This block's share of the per-token quantisation (same rule as
+// quant_tokens_kernel) once every block of the router has the amax of each
+// token: block b codes the 4-element groups g = tid + 256i of the row with
+// g % gridDim.x == b.  xv holds token 0's groups when T == 1.
+__device__ __forceinline__ void quant_share(const RouteSmallArgs &a, const uint2 (&xv)[8],
+                                            const float (*samax)[RS_MAXT])
+{
+    const int tid = threadIdx.x, nb = gridDim.x, b = blockIdx.x;
+    for (int m = 0; m < a.T; ++m) {
+        const float amax = fmaxf(fmaxf(samax[0][m], samax[1][m]), fmaxf(samax[2][m], samax[3][m]));
         float inv = 0.0f, sc = 0.0f;
         if (amax > 0.0f) {
             inv = 127.0f / amax;
             sc = amax / 127.0f;
         }
-        int8_t *qr = xq + (size_t)m * H;
-        for (int i = tid * 8; i < H; i += 2048) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(xr + i);
-            const uint32_t ww[4] = {v.x, v.y, v.z, v.w};
-            uint32_t packed[2] = {0u, 0u};
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float xv = bf16_to_f32((j & 1) ? (ww[j >> 1] >> 16) : (ww[j >> 1] & 0xffffu));
-                const float rr = fminf(fmaxf(rintf(xv * inv), -127.0f), 127.0f);
-                packed[j >> 2] |= ((uint32_t)(int)rr & 0xffu) << (8 * (j & 3));
+        for (int i = 0; i < 8; ++i) {
+            const int g = tid + 256 * i;
+            if (4 * g < a.H && g % nb == b) {
+                const uint2 v = (a.T == 1) ? xv[i]
+                                           : *reinterpret_cast<const uint2 *>(a.x + (size_t)m * a.H + 4 * g);
+                const float f[4] = {bf16_to_f32(v.x & 0xffffu), bf16_to_f32(v.x >> 16),
+                                    bf16_to_f32(v.y & 0xffffu), bf16_to_f32(v.y >> 16)};
+                uint32_t packed = 0u;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float q = fminf(fmaxf(rintf(f[j] * inv), -127.0f), 127.0f);
+                    packed |= ((uint32_t)(int)q & 0xffu) << (8 * j);
+                }
+                *reinterpret_cast<uint32_t *>(a.xq + (size_t)m * a.H + 4 * g) = packed;
             }
-            *reinterpret_cast<uint2 *>(qr + i) = make_uint2(packed[0], packed[1]);
         }
-        if (tid == 0)
-            sa[m] = sc;
+        if (b == 0 && tid == 0)
+            a.sa[m] = sc;
     }
 }
 
 __global__ __launch_bounds__(256) void route_small_kernel(RouteSmallArgs a)
 {
     __shared__ double sred[4][RS_MAXT];
+    __shared__ float samax[4][RS_MAXT];
     __shared__ int32_t s_idx[RS_MAXT * 16];
+    __shared__ double cand_c[64];
+    __shared__ int cand_i[64];
     __shared__ double s_c[1024], s_s[1024], sel_s[16];
     __shared__ uint32_t s_bits[33];
     __shared__ float red[4];
     __shared__ int s_last;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int T = a.T;
+    const bool spread_quant = (a.flags & RS_ROUTER) && (a.flags & RS_QUANT);
+    uint2 xq_v[8];                       // this block's share of token 0 (T == 1)
     if (a.flags & RS_ROUTER) {
         const int e = blockIdx.x;
         // all of this thread's router-row loads first (H <= 8192), then the FMAs
@@ -495,8 +519,6 @@ __global__ __launch_bounds__(256) void route_small_kernel(RouteSmallArgs a)
             const int k0 = tid * 4 + 1024 * i;
             wv[i] = (k0 < a.H) ? *reinterpret_cast<const float4 *>(wr + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        if (blockIdx.x == 0 && (a.flags & RS_QUANT))
-            quant_rows_block(a.x, T, a.H, a.xq, a.sa, red);
         for (int m = 0; m < T; ++m) {
             uint2 xv[NI];
 #pragma unroll
@@ -505,25 +527,46 @@ __global__ __launch_bounds__(256) void route_small_kernel(RouteSmallArgs a)
                 xv[i] = (k0 < a.H) ? *reinterpret_cast<const uint2 *>(a.x + (size_t)m * a.H + k0) : make_uint2(0u, 0u);
             }
             double acc = 0.0;
+            float amax = 0.0f;
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
-                acc = fma((double)bf16_to_f32(xv[i].x & 0xffffu), (double)wv[i].x, acc);
-                acc = fma((double)bf16_to_f32(xv[i].x >> 16), (double)wv[i].y, acc);
-                acc = fma((double)bf16_to_f32(xv[i].y & 0xffffu), (double)wv[i].z, acc);
-                acc = fma((double)bf16_to_f32(xv[i].y >> 16), (double)wv[i].w, acc);
+                const float x0 = bf16_to_f32(xv[i].x & 0xffffu), x1 = bf16_to_f32(xv[i].x >> 16);
+                const float x2 = bf16_to_f32(xv[i].y & 0xffffu), x3 = bf16_to_f32(xv[i].y >> 16);
+                acc = fma((double)x0, (double)wv[i].x, acc);
+                acc = fma((double)x1, (double)wv[i].y, acc);
+                acc = fma((double)x2, (double)wv[i].z, acc);
+                acc = fma((double)x3, (double)wv[i].w, acc);
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3))));
+            }
+            if (m == 0) {
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+                    xq_v[i] = xv[i];
             }
             const double v = wave_sum_d(acc);
-            if (lane == 0)
+            const float am = wave_max(amax);
+            if (lane == 0) {
                 sred[wave][m] = v;
+                samax[wave][m] = am;
+            }
         }
         __syncthreads();
         if (tid < T)
             store_dev(a.logits + (size_t)tid * a.E + e,
                       (sred[0][tid] + sred[1][tid]) + (sred[2][tid] + sred[3][tid]));
-        if (!block_arrives_last(a.done, gridDim.x, &s_last))
+        const bool last = block_arrives_last(a.done, gridDim.x, &s_last);
+        if (!last) {
+            // every block saw all of x: the blocks share its quantisation
+            if (spread_quant)
+                quant_share(a, xq_v, samax);
             return;
+        }
     }
     // ---- the last (or only) block ----
+    if ((a.flags & RS_SEL) && !(a.flags & RS_ROUTER) && tid < a.k) {
+        const int e = a.idx[tid];
+        a.sel[tid] = (e >= 0 && e < a.E) ? a.ptrs[e] : nullptr;
+    }
     if ((a.flags & RS_QUANT) && !(a.flags & RS_ROUTER)) {
         for (int m = 0; m < T; ++m) {
             const uint16_t *xr = a.x + (size_t)m * a.H;
@@ -561,10 +604,18 @@ __global__ __launch_bounds__(256) void route_small_kernel(RouteSmallArgs a)
         }
     }
     if (a.flags & RS_ROUTER) {
-        for (int m = 0; m < T; ++m)
-            topk_rank_block(a.logits + (size_t)m * a.E, a.bias, a.E, a.k, a.r,
-                            a.idx + (size_t)m * a.k, a.w + (size_t)m * a.k, s_idx + m * a.k, s_c,
-                            s_s, sel_s);
+        for (int m = 0; m < T; ++m) {
+            if (a.E <= 256)
+                topk_sort_block(a.logits + (size_t)m * a.E, a.bias, a.E, a.k, a.r,
+                                a.idx + (size_t)m * a.k, a.w + (size_t)m * a.k, s_idx + m * a.k,
+                                s_s, cand_c, cand_i, sel_s);
+            else
+                topk_rank_block(a.logits + (size_t)m * a.E, a.bias, a.E, a.k, a.r,
+                                a.idx + (size_t)m * a.k, a.w + (size_t)m * a.k, s_idx + m * a.k,
+                                s_c, s_s, sel_s);
+        }
+        if (spread_quant)
+            quant_share(a, xq_v, samax);
         if (tid == 0)
             *a.done = 0u;
     } else if (a.flags & RS_LISTS) {
@@ -629,10 +680,70 @@ __global__ __launch_bounds__(256) void route_small_kernel(RouteSmallArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// One token, first of the two router launches (E <= 256, H <= 8192): block e
+// computes the fp64 logit of expert e (same slices and reduction order as
+// route_small_kernel), its sigmoid score s and biased score c (NaN -> -inf)
+// into cs[e] = c, cs[E + e] = s, and codes its share of the token
+// (quant_share).  topk_bs1_kernel then selects.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void router_bs1_kernel(RouteSmallArgs a, double *__restrict__ cs)
+{
+    __shared__ double sred[4];
+    __shared__ float samax[4][RS_MAXT];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int e = blockIdx.x;
+    constexpr int NI = 8;
+    float4 wv[NI];
+    uint2 xv[NI];
+    const float *wr = a.Wr + (size_t)e * a.H;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int k0 = tid * 4 + 1024 * i;
+        wv[i] = (k0 < a.H) ? *reinterpret_cast<const float4 *>(wr + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+        xv[i] = (k0 < a.H) ? *reinterpret_cast<const uint2 *>(a.x + k0) : make_uint2(0u, 0u);
+    }
+    double acc = 0.0;
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const float x0 = bf16_to_f32(xv[i].x & 0xffffu), x1 = bf16_to_f32(xv[i].x >> 16);
+        const float x2 = bf16_to_f32(xv[i].y & 0xffffu), x3 = bf16_to_f32(xv[i].y >> 16);
+        acc = fma((double)x0, (double)wv[i].x, acc);
+        acc = fma((double)x1, (double)wv[i].y, acc);
+        acc = fma((double)x2, (double)wv[i].z, acc);
+        acc = fma((double)x3, (double)wv[i].w, acc);
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3))));
+    }
+    const double v = wave_sum_d(acc);
+    const float am = wave_max(amax);
+    if (lane == 0) {
+        sred[wave] = v;
+        samax[wave][0] = am;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const double L = (sred[0] + sred[1]) + (sred[2] + sred[3]);
+        a.logits[e] = L;
+        const double sv = 1.0 / (1.0 + exp(-L));
+        const double cv = sv + (double)a.bias[e];
+        cs[e] = (cv != cv) ? -INFINITY : cv;
+        cs[a.E + e] = sv;
+    }
+    if (a.flags & RS_QUANT)
+        quant_share(a, xv, samax);
+}
+
+hipError_t launch_router_bs1(const RouteSmallArgs &a, double *cs, hipStream_t st)
+{
+    launch(router_bs1_kernel, a.E, 256, 0, st, a, cs);
+    return hipGetLastError();
+}
+
 hipError_t launch_route_small(const RouteSmallArgs &a, hipStream_t st)
 {
     const int grid = (a.flags & RS_ROUTER) ? a.E : 1;
-    route_small_kernel<<<grid, 256, 0, st>>>(a);
+    launch(route_small_kernel, grid, 256, 0, st, a);
     return hipGetLastError();
 }
 

@@ -2,6 +2,7 @@
 // gfx950 kernels of the quantised MoE layer.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -111,8 +112,29 @@ struct TailArgs {
     uint32_t *ctr;
 };
 
+// One-token expert FFN (kernels_bs1.hip): slot i < k is rank i of the token,
+// slot k the shared expert.
+struct Bs1Args {
+    Experts ex;
+    const void *const *sel;    // [k] blob of each rank (NULL: out of range), or
+                               // NULL to look the blobs up through idx and ex.ptrs
+    const int32_t *idx;        // [k] expert of each rank
+    const float *w;            // [k] gate weights
+    int k, n_shared;
+    const int8_t *xq;          // [H] token codes
+    const float *sa;           // token scale
+    int H, F, group_shift;
+    size_t gu_w, gu_s, gu_tile_w, gu_tile_s, dn_w, dn_s, dn_tile_w, dn_tile_s;
+    float *h;                  // [S][F] SwiGLU rows
+    int8_t *qh;                // [S][F] their codes and scales (written by output block 0)
+    float *sh;
+    float *Y;                  // [S][H] per-slot projections
+    void *out;
+    int out_dtype;
+};
+
 // Few-token routing in one launch (kernels_router.hip).
-enum { RS_ROUTER = 1, RS_QUANT = 2, RS_LISTS = 4 };
+enum { RS_ROUTER = 1, RS_QUANT = 2, RS_LISTS = 4, RS_SEL = 8 };
 constexpr int RS_MAXT = 16;
 
 struct RouteSmallArgs {
@@ -132,7 +154,36 @@ struct RouteSmallArgs {
     int32_t *active, *n_active;
     int n_shared;
     uint32_t *done;
+    // RS_SEL (one token, without the router): sel[i] = ptrs[idx[i]] for the k
+    // ranks (NULL for an id out of range), so the expert kernels find their
+    // blobs with one load instead of two dependent ones
+    const void *const *ptrs;
+    const void **sel;
 };
+
+// ---------------------------------------------------------------------------
+// Kernel timing.  While a profiled launch is enqueued, prof_slot() holds its
+// start/stop events and launch() takes the kernel's own begin and end
+// timestamps from its dispatch (hipExtLaunchKernelGGL), so the measured time
+// is the kernel's, not that of the stream markers around it.
+// ---------------------------------------------------------------------------
+struct ProfSlot {
+    hipEvent_t start = nullptr, stop = nullptr;
+    bool used = false;
+};
+ProfSlot &prof_slot();
+
+template <typename K, typename... Args>
+inline void launch(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t st, Args... args)
+{
+    ProfSlot &p = prof_slot();
+    if (p.start) {
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, p.start, p.stop, 0, args...);
+        p.used = true;
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, args...);
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Launchers (kernels_*.hip).  All enqueue on `st` and return hipGetLastError.
@@ -156,6 +207,13 @@ hipError_t launch_requant(const float *h, int rows, int F, int8_t *q, float *s,
 hipError_t launch_combine(const float *Y, const int32_t *idx, const float *w, int T,
                           int k, int E, int n_shared, int H, void *out, int out_dtype,
                           hipStream_t st);
+bool bs1_supported(int H, int F, int k, int n_shared);
+hipError_t launch_gateup_bs1(const Bs1Args &a, int slots, hipStream_t st);
+hipError_t launch_router_bs1(const RouteSmallArgs &a, double *cs, hipStream_t st);
+hipError_t launch_topk_bs1(const double *cs, int E, float r, const void *const *ptrs,
+                           int32_t *idx_out, float *w_out, const void **sel, const Bs1Args &a,
+                           hipStream_t st);
+hipError_t launch_down_bs1(const Bs1Args &a, hipStream_t st);
 // table[set_idx] = ptr and, when clear_idx >= 0, table[clear_idx] = NULL
 // (one thread; the pointers travel as kernel arguments).
 hipError_t launch_table_update(const void **table, int set_idx, const void *ptr, int clear_idx,

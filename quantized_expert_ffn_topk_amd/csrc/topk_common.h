@@ -1,0 +1,82 @@
+// topk_common.h -- selection of the k best experts of one token on gfx950:
+// the order is the DeepSeek-V3 one (larger biased score first, lower expert
+// index on ties; "Guide Complet de Colibri", table "Points techniques cles",
+// router row).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+namespace moe {
+
+// True when (ca, ia) comes before (cb, ib) in the selection order: larger
+// biased score first, the lower expert index on ties.
+__device__ __forceinline__ bool sel_before(double ca, int ia, double cb, int ib)
+{
+    return ca > cb || (ca == cb && ia < ib);
+}
+
+// Bitonic sort of one (c, i) pair per lane across the 64 lanes of a wave, so
+// that lane 0 holds the first in the selection order, lane 1 the second ...
+__device__ __forceinline__ void wave_sort_sel(double &c, int &ci)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const double oc = __shfl_xor(c, stride, 64);
+            const int oi = __shfl_xor(ci, stride, 64);
+            const bool lower = (lane & stride) == 0;
+            const bool up = (lane & size) == 0 || size == 64;
+            const bool other_first = sel_before(oc, oi, c, ci);
+            if ((lower == up) ? other_first : !other_first) {
+                c = oc;
+                ci = oi;
+            }
+        }
+    }
+}
+
+// Top-k of one token for E <= 256, k <= 16, 256 threads.  Thread e < E holds
+// the biased score c of expert e (NaN already mapped to -inf) and has put its
+// sigmoid score in s_s[e]; other threads hold (-inf, INT_MAX).  Each wave
+// sorts its 64 candidates, wave 0 sorts the first 16 of every wave again.
+// Writes the ranks' ids (s_idx too) and weights w_i = s_i / sum(s) * r, the
+// sum taken in rank order in fp64.
+__device__ __forceinline__ void topk_select_256(double c, int ci, const double *s_s, int k,
+                                                float r, int32_t *__restrict__ idx_out,
+                                                float *__restrict__ w_out, int32_t *s_idx,
+                                                double *cand_c, int *cand_i, double *sel_s)
+{
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    wave_sort_sel(c, ci);                            // s_s is read after the next barrier
+    if (lane < 16) {
+        cand_c[wave * 16 + lane] = c;
+        cand_i[wave * 16 + lane] = ci;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        c = cand_c[lane];
+        ci = cand_i[lane];
+        wave_sort_sel(c, ci);
+        if (lane < k) {
+            s_idx[lane] = ci;
+            sel_s[lane] = s_s[ci];
+        }
+    }
+    __syncthreads();
+    if (tid < k) {
+        double den = 0.0;
+        for (int i = 0; i < k; ++i)
+            den += sel_s[i];
+        const double wi = (den > 0.0) ? (sel_s[tid] / den) * (double)r : 0.0;
+        idx_out[tid] = s_idx[tid];
+        w_out[tid] = (float)wi;
+    }
+    __syncthreads();
+}
+
+}  // namespace moe
