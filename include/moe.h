@@ -286,8 +286,9 @@ moe_status moe_ctx_profile_read(moe_ctx *ctx, double *ms, int64_t *counts);
  * caller-owned, `bytes` long) on `stream`.  which: 0 activation codes [T,H]
  * int8, 1 token scales [T] fp32, 2 router logits [T,E] fp64, 3 SwiGLU outputs h
  * [T,S,F] fp32, 4 requantised h codes [T,S,F] int8, 5 their scales [T,S] fp32,
- * 6 expert outputs Y [T,S,H] fp32; S = k + n_shared slots per token (slot k is
- * the shared expert).  E_INVAL if bytes exceeds the buffer. */
+ * 6 expert outputs Y [T,S,H] fp32, 7 (MXFP4 layers) SwiGLU outputs h as bf16
+ * [T,S,F]; S = k + n_shared slots per token (slot k is the shared expert).
+ * E_INVAL if bytes exceeds the buffer or the buffer does not exist. */
 moe_status moe_debug_read(moe_ctx *ctx, int32_t which, void *dst, size_t bytes,
                           void *stream);
 /* Raw int4 x int8 projection of one packed weight matrix of a blob

@@ -181,7 +181,9 @@ extern "C" moe_status moe_ctx_create(int32_t device, const moe_layer_desc *desc,
     ALLOC(c->zero1, 1);
     ALLOC(c->one1, 1);
     ALLOC(c->dbg_cnt, 1);
-    c->max_tiles = (int)mfma_max_tiles((int)T, (int)E, desc->n_shared);
+    c->max_tiles = (int)(desc->wfmt == MOE_WFMT_MXFP4
+                             ? mx_max_tiles((int)T, (int)E, desc->n_shared, (int)S)
+                             : mfma_max_tiles((int)T, (int)E, desc->n_shared));
     ALLOC(c->tiles, (size_t)c->max_tiles * 2);
     ALLOC(c->n_tiles, 4);
     if (desc->wfmt == MOE_WFMT_MXFP4)
@@ -681,6 +683,7 @@ extern "C" moe_status moe_debug_read(moe_ctx *ctx, int32_t which, void *dst, siz
     case 4: src = ctx->qh; cap = T * S * F; break;
     case 5: src = ctx->sh; cap = T * S * 4; break;
     case 6: src = ctx->Y; cap = T * S * H * 4; break;
+    case 7: src = ctx->hb; cap = ctx->hb ? T * S * F * 2 : 0; break;
     default: return fail(MOE_E_INVAL, "unknown buffer %d", which);
     }
     if (bytes > cap)

@@ -69,6 +69,8 @@ bool use_mfma(const moe_ctx *c, int T);
 // MFMA grouped GEMM path (kernels_gemm.hip)
 hipError_t launch_mfma_tiles(moe_ctx *c, int T, hipStream_t st);
 hipError_t launch_mfma_tiles_single(moe_ctx *c, int T, hipStream_t st);
+// (expert, first row) tiles of mt rows from the routing counts
+hipError_t launch_row_tiles(moe_ctx *c, int mt, hipStream_t st);
 hipError_t launch_gateup_mfma(const ProjArgs &a, const moe_ctx *c, int T, int F, float *h, int ldh,
                               hipStream_t st);
 hipError_t launch_proj_mfma(const ProjArgs &a, const moe_ctx *c, int T, int n_rows,
@@ -76,6 +78,7 @@ hipError_t launch_proj_mfma(const ProjArgs &a, const moe_ctx *c, int T, int n_ro
 size_t mfma_max_tiles(int T, int E, int n_shared);
 
 // MXFP4 path (kernels_mx.hip)
+size_t mx_max_tiles(int T, int E, int n_shared, int S);
 moe_status mx_ffn_enqueue(moe_ctx *c, const void *x, int T, const moe_layer_weights *w,
                           const void *const *expert_ptrs, const int32_t *idx, const float *gw,
                           void *out, hipStream_t st);

@@ -55,18 +55,19 @@ static int tiles_bound(const moe_ctx *c, int T)
 }
 
 // ---------------------------------------------------------------------------
-// Tile list: for experts 0..n_exp-1 in order, ceil(cnt/128) tiles (e, m0).
+// Tile list: for experts 0..n_exp-1 in order, ceil(cnt/mt) tiles (e, m0).
 // One block of 1024 threads; n_exp <= 2048.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void mfma_tiles_kernel(const int32_t *__restrict__ cnt,
-                                                          int n_exp, int2 *__restrict__ tiles,
+                                                          int n_exp, int mt,
+                                                          int2 *__restrict__ tiles,
                                                           int32_t *__restrict__ n_tiles)
 {
     __shared__ int sc[1024];
     const int t = threadIdx.x;
     const int e0 = 2 * t, e1 = 2 * t + 1;
-    const int c0 = e0 < n_exp ? (cnt[e0] + MT - 1) / MT : 0;
-    const int c1 = e1 < n_exp ? (cnt[e1] + MT - 1) / MT : 0;
+    const int c0 = e0 < n_exp ? (cnt[e0] + mt - 1) / mt : 0;
+    const int c1 = e1 < n_exp ? (cnt[e1] + mt - 1) / mt : 0;
     sc[t] = c0 + c1;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
@@ -77,9 +78,9 @@ __global__ __launch_bounds__(1024) void mfma_tiles_kernel(const int32_t *__restr
     }
     int base = sc[t] - c0 - c1;
     for (int j = 0; j < c0; ++j)
-        tiles[base + j] = make_int2(e0, j * MT);
+        tiles[base + j] = make_int2(e0, j * mt);
     for (int j = 0; j < c1; ++j)
-        tiles[base + c0 + j] = make_int2(e1, j * MT);
+        tiles[base + c0 + j] = make_int2(e1, j * mt);
     if (t == 1023)
         *n_tiles = sc[1023];
 }
@@ -87,15 +88,22 @@ __global__ __launch_bounds__(1024) void mfma_tiles_kernel(const int32_t *__restr
 hipError_t launch_mfma_tiles(moe_ctx *c, int T, hipStream_t st)
 {
     (void)T;
-    launch(mfma_tiles_kernel, 1, 1024, 0, st, c->cnt, c->d.n_experts + c->d.n_shared,
+    launch(mfma_tiles_kernel, 1, 1024, 0, st, c->cnt, c->d.n_experts + c->d.n_shared, MT,
                                           reinterpret_cast<int2 *>(c->tiles), c->n_tiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_tiles(moe_ctx *c, int mt, hipStream_t st)
+{
+    launch(mfma_tiles_kernel, 1, 1024, 0, st, c->cnt, c->d.n_experts + c->d.n_shared, mt,
+           reinterpret_cast<int2 *>(c->tiles), c->n_tiles);
     return hipGetLastError();
 }
 
 hipError_t launch_mfma_tiles_single(moe_ctx *c, int T, hipStream_t st)
 {
     (void)T;
-    launch(mfma_tiles_kernel, 1, 1024, 0, st, c->dbg_cnt, 1, reinterpret_cast<int2 *>(c->tiles),
+    launch(mfma_tiles_kernel, 1, 1024, 0, st, c->dbg_cnt, 1, MT, reinterpret_cast<int2 *>(c->tiles),
                                           c->n_tiles);
     return hipGetLastError();
 }
