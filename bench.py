@@ -184,6 +184,158 @@ def run_prefill(args, lay):
     }
 
 
+def run_mx(args):
+    """MXFP4 wide layer: hidden 7168, 384 routed + 1 shared, F 2048, top-8,
+    64 tokens per call, routed scale 1.0, uniform routing bias."""
+    import torch
+    from quantized_expert_ffn_topk_amd import abi, synth
+    from quantized_expert_ffn_topk_amd.layer import Layer, make_desc
+    Hm, Fm, Em, Tm = 7168, 2048, 384, 64
+    t0 = time.time()
+    D = args.mx_distinct
+    distinct = [synth.expert_mxfp4(0, e, Hm, Fm) for e in range(D)]
+    shared = synth.expert_mxfp4(0, -1, Hm, Fm)
+    Wr, _ = synth.router_weights(0, Em, Hm)
+    b = synth.uniform_bias(0, Em)
+    desc = make_desc(Hm, Fm, Em, K_TOP, 1, 32, 1.0, abi.WFMT_MXFP4)
+    lay = Layer(desc, Wr, b, distinct, shared, [e % D for e in range(Em)], max_tokens=Tm)
+    log("mxfp4 layer built in %.1f s" % (time.time() - t0))
+    xs = [lay.x_tensor(synth.activations(20 + i, Tm, Hm)) for i in range(4)]
+    idx, w, out = lay._outs(Tm)
+    stream = torch.cuda.Stream()
+    sh = abi.stream_handle(stream)
+
+    def call(i):
+        abi.moe_layer_forward(lay.ctx, xs[i % 4], Tm, lay.weights, None, 0, idx, w, out, sh)
+
+    for i in range(3):
+        call(i)
+    torch.cuda.synchronize()
+    n = args.mx_calls
+    uniq = []
+    t0 = time.perf_counter()
+    for i in range(n):
+        call(i)
+    stream.synchronize()
+    dt = (time.perf_counter() - t0) / n
+    for i in range(4):                     # experts touched per input
+        call(i)
+        torch.cuda.synchronize()
+        uniq.append(len(np.unique(idx.cpu().numpy())))
+    abi.moe_ctx_profile(lay.ctx, True)
+    abi.moe_ctx_profile_read(lay.ctx)
+    for i in range(n):
+        call(i)
+    torch.cuda.synchronize()
+    prof = abi.moe_ctx_profile_read(lay.ctx)
+    abi.moe_ctx_profile(lay.ctx, False)
+    kus = {k: 1e3 * v[0] / v[1] for k, v in prof.items() if v[1]}
+    blob = abi.moe_blob_bytes(desc)
+    touched = float(np.mean(uniq)) + 1.0
+    layer_bytes = touched * blob + Em * Hm * 4
+    ffn_us = kus.get("gateup", 0.0) + kus.get("down", 0.0)
+    lay.close()
+    return {
+        "workload": "MXFP4 wide layer: hidden 7168, 384 routed + 1 shared experts, FFN 2048, "
+                    "top-8, E2M1 + E8M0 per 32, bf16 activations, 64 tokens per call, routed "
+                    "scale 1.0, bias U(-0.01, 0.01)",
+        "tokens_per_s": Tm / dt,
+        "ms_per_call": 1e3 * dt,
+        "experts_touched_per_call": touched,
+        "hbm": {"bytes_per_call": layer_bytes,
+                "layer_GBs": layer_bytes / dt / 1e9,
+                "layer_frac": layer_bytes / dt / 1e9 / HBM_PEAK_GBS,
+                "expert_ffn_GBs": touched * blob / (ffn_us * 1e-6) / 1e9 if ffn_us else None},
+        "kernels_us": {k: round(v, 2) for k, v in kus.items()},
+    }
+
+
+def run_stream(args, lay, W):
+    """Expert streaming: 16 GLM-shaped layers whose 4096 routed experts live in
+    pinned host memory behind a 24 GiB HBM cache (global LRU), decode batch 1,
+    Zipf(1.1) routing with 70 % layer-to-layer correlation imposed through the
+    selection bias, successor-set lookahead prefetch of the next layer."""
+    import ctypes as C
+    import torch
+    from quantized_expert_ffn_topk_amd import abi, synth
+    L, steps = 16, args.stream_steps
+    blob = abi.moe_blob_bytes(lay.desc)
+    n_phys = args.stream_phys
+    # the 4096 keys alias n_phys pinned blobs: the copy traffic is the same
+    host = abi.moe_host_alloc_pinned(n_phys * blob)
+    try:
+        base = np.ctypeslib.as_array(C.cast(host, C.POINTER(C.c_uint8)), shape=(n_phys * blob,))
+        for i in range(n_phys):
+            base[i * blob:(i + 1) * blob] = lay.blobs[i % len(lay.blobs)].cpu().numpy()
+        ptrs = (C.c_void_p * (L * E))(*[host + ((l * E + e) % n_phys) * blob
+                                         for l in range(L) for e in range(E)])
+        cap = 24 << 30
+        cache = abi.moe_cache_create(abi.moe_cache_desc(0, L, E, blob, cap, C.addressof(ptrs),
+                                                        abi.CACHE_GLOBAL_LRU, abi.CACHE_BACKEND_HIP))
+        demand, predict = synth.zipf_trace(3, L, E, K_TOP, steps)
+        bias = torch.from_numpy(np.stack([[synth.forcing_bias(E, demand[t, l]) for l in range(L)]
+                                          for t in range(steps)])).to(lay.dev)
+        ctx = abi.moe_ctx_create(0, lay.desc, 1)
+        xs = lay.x_tensor(synth.activations(30, steps * L, H))
+        idx, w, out = lay._outs(1)
+        stream = torch.cuda.Stream()
+        sh = abi.stream_handle(stream)
+
+        def layer_call(t, l):
+            wts = abi.moe_layer_weights(lay.Wr.data_ptr(), bias[t, l].data_ptr(), None,
+                                        lay.shared_blob.data_ptr())
+            abi.moe_layer_forward(ctx, xs[t * L + l:t * L + l + 1], 1, wts, cache, l, idx, w, out, sh)
+            if l + 1 < L:
+                abi.moe_cache_stage(cache, l + 1, predict[t, l], abi.STAGE_PREFETCH, sh)
+            abi.moe_cache_release(cache, l, sh)
+
+        warm = min(8, steps // 4)
+        for t in range(warm):
+            for l in range(L):
+                layer_call(t, l)
+        torch.cuda.synchronize()
+        abi.moe_cache_reset_stats(cache)
+        t0 = time.perf_counter()
+        for t in range(warm, steps):
+            for l in range(L):
+                layer_call(t, l)
+        stream.synchronize()
+        dt = time.perf_counter() - t0
+        st = abi.moe_cache_stats_get(cache)
+        abi.moe_ctx_destroy(ctx)
+        abi.moe_cache_destroy(cache)
+    finally:
+        abi.moe_host_free_pinned(host)
+    # pinned host -> device ceiling on this box, same blob size
+    src = torch.empty(blob * 32, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(blob * 32, dtype=torch.uint8, device=lay.dev)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(3):
+        dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    ceil_gbs = 3 * blob * 32 / (time.perf_counter() - t1) / 1e9
+    n = steps - warm
+    dem = st["demand_hits"] + st["demand_misses"]
+    return {
+        "workload": "expert streaming: 16 GLM-shaped layers, 4096 routed experts of %d B in "
+                    "pinned host memory (keys aliased onto %d physical blobs), 24 GiB HBM LRU "
+                    "pool (%d slots), decode batch 1, Zipf(1.1) routing with 0.7 layer-to-layer "
+                    "correlation, lookahead prefetch of the successor set" % (blob, n_phys,
+                                                                               st["n_slots"]),
+        "tokens_per_s": n / dt,
+        "ms_per_token": 1e3 * dt / n,
+        "h2d_GBs": st["bytes_copied"] / dt / 1e9,
+        "h2d_pinned_ceiling_GBs": ceil_gbs,
+        "demand_hit_rate": st["demand_hits"] / dem if dem else None,
+        "prefetch_precision": (st["prefetch_used"] / st["prefetch_issued"]
+                               if st["prefetch_issued"] else None),
+        "misses_per_token": st["demand_misses"] / n,
+        "stats": st,
+    }
+
+
 def cpu_baseline(args, lay, W):
     """The plain C oracle (single thread) on a bounded sample of decode steps."""
     import oracle
@@ -229,6 +381,12 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-tokens", type=int, default=4096)
     ap.add_argument("--prefill-calls", type=int, default=5)
+    ap.add_argument("--no-mx", action="store_true")
+    ap.add_argument("--no-stream", action="store_true")
+    ap.add_argument("--stream-steps", type=int, default=96)
+    ap.add_argument("--stream-phys", type=int, default=48)
+    ap.add_argument("--mx-calls", type=int, default=10)
+    ap.add_argument("--mx-distinct", type=int, default=4)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -302,6 +460,10 @@ def main():
     }
     if not args.no_prefill:
         line["prefill"] = run_prefill(args, lay)
+    if not args.no_stream:
+        line["streaming"] = run_stream(args, lay, W)
+    if not args.no_mx:
+        line["mxfp4"] = run_mx(args)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args, lay, W)
     else:
