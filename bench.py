@@ -49,6 +49,25 @@ def dn_section_bytes(H_, F_, g):
     return H_ * F_ // 2 + (H_ // 16) * (F_ // g) * 32
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_glm_bs1_hbm_traffic.md")
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter
+    summary, or None when a kernel source listed there has changed since."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_RECORD).read()
+        rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+        for path, digest in rec["sources_sha256"].items():
+            with open(os.path.join(ROOT, path), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != digest:
+                    return None
+        return rec["traffic_bytes_per_launch"]
+    except (OSError, IndexError, KeyError, ValueError):
+        return None
+
+
 def build_layer(args):
     from quantized_expert_ffn_topk_amd import abi, synth
     from quantized_expert_ffn_topk_amd.layer import Layer, make_desc
@@ -381,6 +400,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-tokens", type=int, default=4096)
     ap.add_argument("--prefill-calls", type=int, default=5)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB (HBM counter "
+                         "calibration under rocprofv3 --pmc)")
     ap.add_argument("--no-mx", action="store_true")
     ap.add_argument("--no-stream", action="store_true")
     ap.add_argument("--stream-steps", type=int, default=96)
@@ -400,6 +422,16 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     lay, W = build_layer(args)
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=lay.dev)
+        b = torch.empty(n, dtype=torch.uint8, device=lay.dev)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("calibration copy of %d MiB done" % args.calib_copy_mib)
+        del a, b
     res = run_decode(args, lay)
     K = args.steps
     best = min(res["eager_s"], res.get("graph_s", 1e30))
@@ -442,7 +474,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(),
             "bytes_per_launch": gu_bytes,
             "avg_us": gu_us,
         },
