@@ -14,11 +14,11 @@
 //
 //   gateup_bs1_kernel : block (slot, b) = 2 waves, the gate tile 2b and the up
 //                       tile 2b+1 over all of K = hidden; SwiGLU of the 16 rows.
-//   down_bs1_kernel   : block = 32 output rows, one wave per slot.  Each wave
-//                       requantises its slot's SwiGLU row (same rule as the
-//                       token quantisation) into LDS, projects both 16-row
+//   down_bs1_kernel   : block = 16 or 32 output rows, one wave per slot.  Each
+//                       wave requantises its slot's SwiGLU row (same rule as
+//                       the token quantisation) into LDS, projects the 16-row
 //                       tiles, and the block then combines
-//                       the slots of the 32 outputs: shared expert first, then
+//                       the slots of its outputs: shared expert first, then
 //                       rank order, in fp64, rounded once.  No cross-block
 //                       hand-off inside a kernel.
 #include "device_common.h"
@@ -197,8 +197,8 @@ __global__ __launch_bounds__(256) void topk_bs1_kernel(const double *__restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Down projection + combine for output rows [32p, 32p + 32): the two 16-row
-// tiles 2p, 2p+1 of every slot.  F <= 2048.  Each wave codes its slot's
+// Down projection + combine for the TPW 16-row tiles TPW*p, ... of every
+// slot (output rows [16*TPW*p, 16*TPW*(p+1))).  F <= 2048.  Each wave codes its slot's
 // SwiGLU row with the token quantisation rule (amax over the row, inv =
 // 127/amax, s = amax/127, q = rint(h*inv) clamped to [-127, 127]) into LDS,
 // then streams both tiles with two batches of U loads in flight.
@@ -214,11 +214,11 @@ __device__ __forceinline__ void bs1_load2(const uint4 *wp, const uint16_t *sp, s
         bs1_load<U>(wp + wstep, sp + sstep, sstride, j - nj, wv, sv);
 }
 
-template <int U, int NW, bool DB>
+template <int U, int NW, bool DB, int TPW>
 __global__ __launch_bounds__(64 * NW) void down_bs1_kernel(Bs1Args a)
 {
     extern __shared__ __align__(16) unsigned char smem[];   // S rows of F codes
-    __shared__ float sY[16][32];
+    __shared__ float sY[16][16 * TPW];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, c4 = lane >> 4, gs = a.group_shift;
     const int ai = wave, pr = blockIdx.x;
@@ -243,13 +243,13 @@ __global__ __launch_bounds__(64 * NW) void down_bs1_kernel(Bs1Args a)
             hv[i] = hr[lane + 64 * i];
     const uint8_t *blob = bs1_slot_blob(a, ai);
     if (blob) {
-        wp = reinterpret_cast<const uint4 *>(blob + a.dn_w + (size_t)(2 * pr) * a.dn_tile_w) + lane;
-        sp = reinterpret_cast<const uint16_t *>(blob + a.dn_s + (size_t)(2 * pr) * a.dn_tile_s) +
+        wp = reinterpret_cast<const uint4 *>(blob + a.dn_w + (size_t)(TPW * pr) * a.dn_tile_w) + lane;
+        sp = reinterpret_cast<const uint16_t *>(blob + a.dn_s + (size_t)(TPW * pr) * a.dn_tile_s) +
              (((c4 >> gs) << 4) + r);
         wstep = a.dn_tile_w >> 4;
         sstep = a.dn_tile_s >> 1;
         bs1_load<U>(wp, sp, sstride, 0, wa, sa);
-        if (DB)
+        if (DB && U < TPW * nj)
             bs1_load2<U>(wp, sp, wstep, sstep, sstride, U, nj, wb, sb);
 
         float amax = 0.0f;
@@ -287,9 +287,9 @@ __global__ __launch_bounds__(64 * NW) void down_bs1_kernel(Bs1Args a)
         __builtin_amdgcn_wave_barrier();
     }
     if (blob) {
-        // batches j0 = 0, U, 2U, ... over both tiles (U divides nj, so no batch
-        // straddles them); two in flight: compute one while the next loads
-        const int nb = 2 * nj;
+        // batches j0 = 0, U, 2U, ... over the wave's tiles (U divides nj, so no
+        // batch straddles two tiles)
+        const int nb = TPW * nj;
         double p = 0.0, p0 = 0.0;                  // p: the tile being summed
         if (DB) {
             // two batches in flight: compute one while the next loads
@@ -302,6 +302,8 @@ __global__ __launch_bounds__(64 * NW) void down_bs1_kernel(Bs1Args a)
                 if (j0 + 2 * U < nb)
                     bs1_load2<U>(wp, sp, wstep, sstep, sstride, j0 + 2 * U, nj, wa, sa);
                 const int j1 = j0 + U;
+                if (j1 >= nb)
+                    break;
                 if (j1 == nj) {
                     p0 = p;
                     p = 0.0;
@@ -322,21 +324,28 @@ __global__ __launch_bounds__(64 * NW) void down_bs1_kernel(Bs1Args a)
             }
         }
         double p1 = p;
+        if (TPW == 1)
+            p0 = p;
         p0 += shfl_xor_d(p0, 16);
         p0 += shfl_xor_d(p0, 32);
-        p1 += shfl_xor_d(p1, 16);
-        p1 += shfl_xor_d(p1, 32);
+        if (TPW == 2) {
+            p1 += shfl_xor_d(p1, 16);
+            p1 += shfl_xor_d(p1, 32);
+        }
         if (lane < 16) {
-            const float y0 = (float)(p0 * (double)sc), y1 = (float)(p1 * (double)sc);
+            float *yg = a.Y + (size_t)ai * a.H + 16 * TPW * pr;
+            const float y0 = (float)(p0 * (double)sc);
             sY[ai][r] = y0;
-            sY[ai][16 + r] = y1;
-            float *yg = a.Y + (size_t)ai * a.H + 32 * pr;
             yg[r] = y0;
-            yg[16 + r] = y1;
+            if (TPW == 2) {
+                const float y1 = (float)(p1 * (double)sc);
+                sY[ai][16 + r] = y1;
+                yg[16 + r] = y1;
+            }
         }
     }
     __syncthreads();
-    if (threadIdx.x < 32) {
+    if (threadIdx.x < 16 * TPW) {
         double o = a.n_shared ? (double)sY[a.k][threadIdx.x] : 0.0;
         for (int i = 0; i < a.k; ++i) {
             const int ex = a.idx[i];
@@ -344,7 +353,7 @@ __global__ __launch_bounds__(64 * NW) void down_bs1_kernel(Bs1Args a)
                 o = fma((double)a.w[i], (double)sY[i][threadIdx.x], o);
         }
         const float f = (float)o;
-        const size_t n = (size_t)32 * pr + threadIdx.x;
+        const size_t n = (size_t)16 * TPW * pr + threadIdx.x;
         if (a.out_dtype == MOE_DT_BF16)
             reinterpret_cast<uint16_t *>(a.out)[n] = f32_to_bf16(f);
         else
@@ -414,17 +423,25 @@ hipError_t launch_topk_bs1(const double *cs, int E, float r, const void *const *
     return hipGetLastError();
 }
 
+#ifndef MOE_BS1_DOWN_TPW
+#define MOE_BS1_DOWN_TPW 2
+#endif
+#ifndef MOE_BS1_DOWN_U
+#define MOE_BS1_DOWN_U 2
+#endif
+
 hipError_t launch_down_bs1(const Bs1Args &a, hipStream_t st)
 {
+    constexpr int TPW = MOE_BS1_DOWN_TPW;
     const int S = a.k + a.n_shared;
-    const dim3 grid(a.H / 32);
+    const dim3 grid(a.H / (16 * TPW));
     const size_t lds = (size_t)S * a.F;
     // two batches of 2 loads in flight per wave next to the SwiGLU row: for up
     // to 9 slots the block may use 3 waves per SIMD, for up to 16 slots 4
     if (S <= 9)
-        launch(down_bs1_kernel<2, 9, true>, grid, 64 * S, lds, st, a);
+        launch(down_bs1_kernel<MOE_BS1_DOWN_U, 9, true, TPW>, grid, 64 * S, lds, st, a);
     else
-        launch(down_bs1_kernel<2, 16, true>, grid, 64 * S, lds, st, a);
+        launch(down_bs1_kernel<2, 16, true, TPW>, grid, 64 * S, lds, st, a);
     return hipGetLastError();
 }
 

@@ -74,7 +74,7 @@ hipError_t launch_quant_tokens(const uint16_t *x, int T, int H, int8_t *q, float
 // Router logits l[t,e] = sum_k x[t,k]*Wr[e,k] in fp64 (bf16 x fp32 products
 // are exact in fp64).
 // Few tokens: one wave per expert streams its router row with 16-byte loads
-// for up to TB tokens.  Many tokens: 64x64 output tiles through LDS.
+// for up to TB tokens.  Many tokens: the fp64 MFMA below.
 // ---------------------------------------------------------------------------
 template <int TB>
 __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t *__restrict__ x, int T,
@@ -112,57 +112,86 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t *__rest
     }
 }
 
-// 64 tokens x 64 experts per block, each thread a 4x4 register tile; K in
-// steps of 32 through LDS (values widened to fp64 once, on the way in).
-__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__restrict__ x, int T,
-                                                          int H, const float *__restrict__ Wr,
-                                                          int E, double *__restrict__ logits)
+// Many tokens on the fp64 MFMA (v_mfma_f64_16x16x4_f64; checked on the
+// device: lane l supplies A[l%16][l/16] and B[l/16][l%16], result register i
+// of lane l is D[l/16 + 4i][l%16]).  A wave computes MT tiles of 16 tokens
+// against one tile of 16 experts over a K slice; the block's KS waves take KS
+// consecutive slices and their partial sums are added in slice order.  Every
+// product of a bf16 input and an fp32 weight is exact in fp64.  For each 32
+// inputs, lane group g = l/16 loads inputs 8g..8g+7 of its token row and its
+// router row, and MFMA j takes element j of them: the 32 products are summed
+// in an order fixed by the kernel.
+template <int MT, int KS>
+__global__ __launch_bounds__(64 * KS) void router_mfma_kernel(const uint16_t *__restrict__ x,
+                                                              int T, int H,
+                                                              const float *__restrict__ Wr,
+                                                              int E, double *__restrict__ logits)
 {
-    constexpr int TM = 64, TN = 64, KS = 32;
-    __shared__ double xs[KS][TM + 1];
-    __shared__ double ws[KS][TN + 1];
-    const int tm0 = blockIdx.y * TM, tn0 = blockIdx.x * TN;
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;   // 16 x 16 threads
-    double acc[4][4];
+    typedef double f64x4 __attribute__((ext_vector_type(4)));
+    __shared__ double part[KS > 1 ? KS : 1][MT][4][64];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16 * MT;
+    const int KL = H / KS, kb = wave * KL;
+    const float *wrow = Wr + (size_t)min(e0 + r, E - 1) * H + kb + 8 * g;   // clamped rows
+    const uint16_t *xrow[MT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int m = 0; m < MT; ++m)
+        xrow[m] = x + (size_t)min(t0 + 16 * m + r, T - 1) * H + kb + 8 * g;
+    f64x4 acc[MT];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = 0.0;
-    for (int k0 = 0; k0 < H; k0 += KS) {
-        // load 64 x 32 of x and of Wr: 2048 values each, 8 per thread
+    for (int m = 0; m < MT; ++m)
+        acc[m] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int k = 0; k < KL; k += 32) {
+        const float4 w0 = *reinterpret_cast<const float4 *>(wrow + k);
+        const float4 w1 = *reinterpret_cast<const float4 *>(wrow + k + 4);
+        uint4 xv[MT];
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            int v = threadIdx.x + it * 256;
-            int row = v >> 5, kk = v & 31;
-            int t = tm0 + row, e = tn0 + row;
-            xs[kk][row] = (t < T) ? (double)bf16_to_f32(x[(size_t)t * H + k0 + kk]) : 0.0;
-            ws[kk][row] = (e < E) ? (double)Wr[(size_t)e * H + k0 + kk] : 0.0;
-        }
-        __syncthreads();
-#pragma unroll 4
-        for (int kk = 0; kk < KS; ++kk) {
-            double a[4], b[4];
+        for (int m = 0; m < MT; ++m)
+            xv[m] = *reinterpret_cast<const uint4 *>(xrow[m] + k);
+        const float wf[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                a[i] = xs[kk][ty + 16 * i];
-                b[i] = ws[kk][tx + 16 * i];
+        for (int j = 0; j < 8; ++j) {
+            const double b = (double)wf[j];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const uint32_t d = (j >> 1) == 0 ? xv[m].x : (j >> 1) == 1 ? xv[m].y
+                                 : (j >> 1) == 2 ? xv[m].z : xv[m].w;
+                const double a = (double)bf16_to_f32((j & 1) ? (d >> 16) : (d & 0xffffu));
+                acc[m] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[m], 0, 0, 0);
             }
+        }
+    }
+    if (KS > 1) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = fma(a[i], b[j], acc[i][j]);
-        }
+                part[wave][m][i][lane] = acc[m][i];
         __syncthreads();
+        if (wave != 0)
+            return;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                double v = part[0][m][i][lane];
+#pragma unroll
+                for (int q = 1; q < KS; ++q)
+                    v += part[q][m][i][lane];
+                acc[m][i] = v;
+            }
     }
+    const int e = e0 + r;
+    if (e >= E)
+        return;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int t = tm0 + ty + 16 * i, e = tn0 + tx + 16 * j;
-            if (t < T && e < E)
-                logits[(size_t)t * E + e] = acc[i][j];
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 16 * m + g + 4 * i;
+            if (t < T)
+                logits[(size_t)t * E + e] = acc[m][i];
         }
 }
 
@@ -174,9 +203,26 @@ hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *Wr
     if (T <= 16) {
         dim3 grid((E + 3) / 4, (T + 3) / 4);
         launch(router_gemv_kernel<4>, grid, 256, 0, st, x, T, H, Wr, E, logits);
+        return hipGetLastError();
+    }
+    // enough waves to fill the chip: 64-token tiles with 1-2 K slices for many
+    // tokens, 16-token tiles with up to 16 slices for few (H/32 is a multiple
+    // of 8, so 1, 2, 4 and 8 slices of whole 32-input steps always exist)
+    const int ne = (E + 15) / 16, H32 = H / 32;
+    if (T >= 1024) {
+        dim3 grid(ne, (T + 63) / 64);
+        const long tiles = (long)grid.x * grid.y;
+        if (tiles >= 2048)
+            launch(router_mfma_kernel<4, 1>, grid, 64, 0, st, x, T, H, Wr, E, logits);
+        else
+            launch(router_mfma_kernel<4, 2>, grid, 128, 0, st, x, T, H, Wr, E, logits);
     } else {
-        dim3 grid((E + 63) / 64, (T + 63) / 64);
-        launch(router_gemm_kernel, grid, 256, 0, st, x, T, H, Wr, E, logits);
+        dim3 grid(ne, (T + 15) / 16);
+        const long tiles = (long)grid.x * grid.y;
+        if (tiles >= 512 || H32 % 16)
+            launch(router_mfma_kernel<1, 8>, grid, 512, 0, st, x, T, H, Wr, E, logits);
+        else
+            launch(router_mfma_kernel<1, 16>, grid, 1024, 0, st, x, T, H, Wr, E, logits);
     }
     return hipGetLastError();
 }

@@ -248,3 +248,17 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
     del g
     lay.close()
+
+
+@pytest.mark.parametrize("T,E", [(17, 40), (100, 64), (300, 256), (1100, 48)])
+def test_router_logits_many_tokens(T, E):
+    # the fp64 MFMA router (more than 16 tokens), E not a multiple of 16 included
+    c = Case(30 + T, T, 1024, 256, E, 6, 0, n_distinct=1)
+    lay = c.layer()
+    idx, w = lay.router(lay.x_tensor(c.x))
+    torch.cuda.synchronize()
+    idx_o, w_o, lg_o, sc_o, ch_o = c.oracle_router()
+    check_routing(idx.cpu().numpy(), w.cpu().numpy(), idx_o, w_o, ch_o)
+    lg = lay.debug_read(2, (T, E), torch.float64).cpu().numpy()
+    np.testing.assert_allclose(lg, lg_o, rtol=1e-12, atol=1e-13)
+    lay.close()
