@@ -123,16 +123,6 @@ __device__ __forceinline__ void block_coords(int mt_max, int *nb, int *mt)
     *mt = logical - *nb * mt_max;
 }
 
-__device__ __forceinline__ v4i nibble_bytes(uint4 w, int shift)
-{
-    v4i b;
-    b[0] = (int)((w.x << shift) & 0xf0f0f0f0u);
-    b[1] = (int)((w.y << shift) & 0xf0f0f0f0u);
-    b[2] = (int)((w.z << shift) & 0xf0f0f0f0u);
-    b[3] = (int)((w.w << shift) & 0xf0f0f0f0u);
-    return b;
-}
-
 __device__ __forceinline__ v4i as_v4i(uint4 w)
 {
     v4i b;
@@ -144,65 +134,6 @@ __device__ __forceinline__ v4i as_v4i(uint4 w)
 }
 
 // ---------------------------------------------------------------------------
-// One kernel body for both projections.  A block owns a tile of up to 128
-// activation rows of one expert and 128 weight rows:
-//   GATEUP: gate rows n and up rows n for n in [64nb, 64nb+64), output
-//           h = fp32(silu(G)*U) (G, U scaled by the token scale);
-//   PROJ  : weight rows [128nb, 128nb+128) (down projection, or one part of
-//           the gate/up section), output fp32(sum * row scale).
-// K is walked in stages of 4 chunks (128 inputs).  Each stage's activation
-// rows (128 x 128 B) and weight nibbles (128 x 64 B) are staged in LDS, double
-// buffered, rows padded so that 16-byte LDS reads are free of bank conflicts.
-// Wave w: weight-row blocks rb0, rb1 (32 rows each) and activation-row blocks
-// 2*(w>>1), 2*(w>>1)+1: four MFMAs per chunk; empty activation blocks of a
-// partly filled tile are skipped.
-// ---------------------------------------------------------------------------
-constexpr int KB = 4;                      // chunks per stage
-constexpr int A_LD = KB * 32 + 16;         // LDS row pitch of activations (bytes)
-constexpr int B_LD = KB * 16 + 16;         // LDS row pitch of weight nibbles
-constexpr int A_STAGE = MT * A_LD;
-constexpr int B_STAGE = 128 * B_LD;
-
-// One stage (KB chunks) of one wave: its activation block (32 rows) against
-// the lane's two weight rows.  Per scale group: MFMA into a fresh int32 tile,
-// then the exact fp64 epilogue acc += (int32 result) * scale/16.
-template <int GS>
-__device__ __forceinline__ void stage_compute(const uint8_t *__restrict__ A,
-                                              const uint8_t *__restrict__ B, int arow, int R0,
-                                              int R1, int hh, int shift, const uint16_t *sv0,
-                                              const uint16_t *sv1, double (&acc)[2][16])
-{
-#pragma unroll
-    for (int u = 0; u < KB; u += GS) {
-        const double s0 = (double)f16_to_f32(sv0[u / GS]) * 0.0625;
-        const double s1 = (double)f16_to_f32(sv1[u / GS]) * 0.0625;
-        v4i a[GS];
-#pragma unroll
-        for (int v = 0; v < GS; ++v)
-            a[v] = as_v4i(*reinterpret_cast<const uint4 *>(A + arow * A_LD + (u + v) * 32 + 16 * hh));
-        const v16i zero = {0};
-        v16i d = zero;
-#pragma unroll
-        for (int v = 0; v < GS; ++v)
-            d = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                a[v], nibble_bytes(*reinterpret_cast<const uint4 *>(B + R0 * B_LD + (u + v) * 16), shift),
-                d, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            acc[0][r] = fma((double)d[r], s0, acc[0][r]);
-        d = zero;
-#pragma unroll
-        for (int v = 0; v < GS; ++v)
-            d = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                a[v], nibble_bytes(*reinterpret_cast<const uint4 *>(B + R1 * B_LD + (u + v) * 16), shift),
-                d, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            acc[1][r] = fma((double)d[r], s1, acc[1][r]);
-    }
-}
-
-// ---------------------------------------------------------------------------
 // One kernel body for both projections.  A block (8 waves) owns a tile of up
 // to 128 activation rows of one expert and 128 weight rows:
 //   GATEUP: gate rows n and up rows n for n in [64nb, 64nb+64), output
@@ -210,20 +141,32 @@ __device__ __forceinline__ void stage_compute(const uint8_t *__restrict__ A,
 //   PROJ  : weight rows [128nb, 128nb+128) (down projection, or one part of
 //           the gate/up section), output fp32(sum * row scale).
 // K is walked in stages of 4 chunks (128 inputs).  Each stage's activation
-// rows (128 x 128 B) and weight nibbles (128 x 64 B) are staged in LDS, double
-// buffered, rows padded so that 16-byte LDS reads are free of bank conflicts.
+// rows (128 x 128 B), its weights already widened from nibbles to the signed
+// bytes 16q (128 x 128 B) and its group scales / 16 as fp32 are staged in LDS,
+// double buffered, rows padded so that 16-byte LDS reads are free of bank
+// conflicts.  Widening and scale conversion happen once per block in the
+// staging, so the waves' VALU work is the exact epilogue alone.
 // Wave w: activation block w&3 (32 rows) and weight blocks rb0, rb1 (32 rows
 // each): two MFMAs per chunk.  Waves whose block is past the expert's rows
-// only help staging.
+// only help staging.  80 KB of LDS: two blocks per CU.
 // ---------------------------------------------------------------------------
+constexpr int KB = 4;                      // chunks per stage
+constexpr int A_LD = KB * 32 + 16;         // LDS row pitch of activations (bytes)
+constexpr int B_LD = KB * 32 + 16;         // LDS row pitch of widened weights
+constexpr int A_STAGE = MT * A_LD;
+constexpr int B_STAGE = 128 * B_LD;
+constexpr int S_STAGE = 128 * KB;          // fp32 scales / 16 per stage (GS = 1)
+
 template <bool GATEUP, int GS>
-__global__ __launch_bounds__(512, 1) void mfma_proj_kernel(ProjArgs a, const int2 *__restrict__ tiles,
+__global__ __launch_bounds__(512)
+void mfma_proj_kernel(ProjArgs a, const int2 *__restrict__ tiles,
                                                            const int32_t *__restrict__ n_tiles,
                                                            int mt_max, int n_blocks,
                                                            float *__restrict__ out, int ldo)
 {
     __shared__ __align__(16) uint8_t lds_a[2 * A_STAGE];
     __shared__ __align__(16) uint8_t lds_b[2 * B_STAGE];
+    __shared__ float lds_s[2 * S_STAGE];
     __shared__ int s_slot[MT], s_row[MT];
     __shared__ float s_sc[MT];
     __shared__ int s_tile[8];
@@ -267,23 +210,34 @@ __global__ __launch_bounds__(512, 1) void mfma_proj_kernel(ProjArgs a, const int
     const uint8_t *qbase = reinterpret_cast<const uint8_t *>(a.q);
 
     // global -> LDS assignment: activations 1024 pieces of 16 B (2/thread),
-    // weights 512 pieces (1/thread)
-    const uint8_t *ga[2];
-    int la[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int p = tid + 512 * j;
-        const int tok = p >> 3, seg = p & 7;
-        const int row = s_row[tok];
-        ga[j] = qbase + (size_t)(row < 0 ? s_row[0] : row) * K + seg * 16;
-        la[j] = tok * A_LD + seg * 16;
+    // weight nibbles 512 pieces (1/thread, widened to 32 B), scales 128 rows x
+    // KB/GS groups (one per thread for the first 128*KB/GS threads)
+    const uint8_t *ga0, *ga1;
+    int la0, la1;
+    {
+        const int tok0 = tid >> 3, tok1 = (tid + 512) >> 3, seg = tid & 7;
+        const int row0 = s_row[tok0], row1 = s_row[tok1];
+        ga0 = qbase + (size_t)(row0 < 0 ? s_row[0] : row0) * K + seg * 16;
+        ga1 = qbase + (size_t)(row1 < 0 ? s_row[0] : row1) * K + seg * 16;
+        la0 = tok0 * A_LD + seg * 16;
+        la1 = tok1 * A_LD + seg * 16;
     }
     const uint8_t *gb;
     int lb;
     {
         const int r = tid & 15, kcl = (tid >> 4) & 3, tj = tid >> 6;
         gb = blob + a.w_off + (size_t)s_tile[tj] * a.tile_w + kcl * 256 + r * 16;
-        lb = (16 * tj + r) * B_LD + kcl * 16;
+        lb = (16 * tj + r) * B_LD + kcl * 32;
+    }
+    constexpr int NG = KB / GS;                // scale groups per stage
+    const bool s_thread = tid < 128 * NG;
+    const uint16_t *gs_ = nullptr;
+    int ls_ = 0;
+    if (s_thread) {
+        const int row = tid / NG, u = tid % NG;
+        gs_ = reinterpret_cast<const uint16_t *>(blob + a.s_off + (size_t)s_tile[row >> 4] * a.tile_s) +
+              u * 16 + (row & 15);
+        ls_ = row * KB + u;
     }
 
     const int wave = tid >> 6, lane = tid & 63;
@@ -292,11 +246,7 @@ __global__ __launch_bounds__(512, 1) void mfma_proj_kernel(ProjArgs a, const int
     const int rb0 = GATEUP ? np : 2 * np;
     const int rb1 = GATEUP ? 2 + np : 2 * np + 1;
     const bool active = __builtin_amdgcn_readfirstlane(32 * mb < mc ? 1 : 0) != 0;
-    // scales of this lane's two weight rows
     const int R0 = 32 * rb0 + li, R1 = 32 * rb1 + li;
-    const uint16_t *sp0 = reinterpret_cast<const uint16_t *>(blob + a.s_off + (size_t)s_tile[R0 >> 4] * a.tile_s) + (R0 & 15);
-    const uint16_t *sp1 = reinterpret_cast<const uint16_t *>(blob + a.s_off + (size_t)s_tile[R1 >> 4] * a.tile_s) + (R1 & 15);
-    const int shift = hh ? 0 : 4;
     const int arow = 32 * mb + li;
 
     double acc[2][16];
@@ -306,42 +256,72 @@ __global__ __launch_bounds__(512, 1) void mfma_proj_kernel(ProjArgs a, const int
         for (int r = 0; r < 16; ++r)
             acc[i][r] = 0.0;
 
-    uint4 ra[2], rbv;
-    auto gload = [&](int stage) {
-        const size_t ko = (size_t)stage * KB;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            ra[j] = *reinterpret_cast<const uint4 *>(ga[j] + ko * 32);
-        rbv = *reinterpret_cast<const uint4 *>(gb + ko * 256);
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            *reinterpret_cast<uint4 *>(lds_a + buf * A_STAGE + la[j]) = ra[j];
-        *reinterpret_cast<uint4 *>(lds_b + buf * B_STAGE + lb) = rbv;
-    };
+    uint4 ra0, ra1, rbv;
+    uint16_t rs = 0;
+#define GLOAD(stage)                                                              \
+    do {                                                                          \
+        const size_t ko_ = (size_t)(stage) * KB;                                  \
+        ra0 = *reinterpret_cast<const uint4 *>(ga0 + ko_ * 32);                   \
+        ra1 = *reinterpret_cast<const uint4 *>(ga1 + ko_ * 32);                   \
+        rbv = *reinterpret_cast<const uint4 *>(gb + ko_ * 256);                   \
+        if (s_thread)                                                             \
+            rs = gs_[(size_t)(stage) * NG * 16];                                  \
+    } while (0)
+    // nibble j of a byte: low = input j, high = input j+16 (4-bit two's
+    // complement); masked into the top of a byte it is the signed byte 16q
+#define LSTORE(buf)                                                               \
+    do {                                                                          \
+        *reinterpret_cast<uint4 *>(lds_a + (buf) * A_STAGE + la0) = ra0;          \
+        *reinterpret_cast<uint4 *>(lds_a + (buf) * A_STAGE + la1) = ra1;          \
+        *reinterpret_cast<uint4 *>(lds_b + (buf) * B_STAGE + lb) =                \
+            make_uint4((rbv.x << 4) & 0xf0f0f0f0u, (rbv.y << 4) & 0xf0f0f0f0u,    \
+                       (rbv.z << 4) & 0xf0f0f0f0u, (rbv.w << 4) & 0xf0f0f0f0u);   \
+        *reinterpret_cast<uint4 *>(lds_b + (buf) * B_STAGE + lb + 16) =           \
+            make_uint4(rbv.x & 0xf0f0f0f0u, rbv.y & 0xf0f0f0f0u,                  \
+                       rbv.z & 0xf0f0f0f0u, rbv.w & 0xf0f0f0f0u);                 \
+        if (s_thread)                                                             \
+            lds_s[(buf) * S_STAGE + ls_] = f16_to_f32(rs) * 0.0625f; /* exact */  \
+    } while (0)
 
-    gload(0);
-    lstore(0);
+    GLOAD(0);
+    LSTORE(0);
     __syncthreads();
     for (int st = 0; st < n_stages; ++st) {
         const int buf = st & 1;
         if (st + 1 < n_stages)
-            gload(st + 1);
+            GLOAD(st + 1);
         if (active) {
-            uint16_t sv0[KB / GS], sv1[KB / GS];
+            const uint8_t *A = lds_a + buf * A_STAGE + arow * A_LD + 16 * hh;
+            const uint8_t *B0 = lds_b + buf * B_STAGE + R0 * B_LD + 16 * hh;
+            const uint8_t *B1 = lds_b + buf * B_STAGE + R1 * B_LD + 16 * hh;
+            const float *S0 = lds_s + buf * S_STAGE + R0 * KB;
+            const float *S1 = lds_s + buf * S_STAGE + R1 * KB;
 #pragma unroll
-            for (int u = 0; u < KB / GS; ++u) {
-                sv0[u] = sp0[(size_t)(st * (KB / GS) + u) * 16];
-                sv1[u] = sp1[(size_t)(st * (KB / GS) + u) * 16];
+            for (int u = 0; u < KB; u += GS) {
+                const v16i zero = {0};
+                v16i d0 = zero, d1 = zero;
+#pragma unroll
+                for (int v = 0; v < GS; ++v) {
+                    const v4i av = as_v4i(*reinterpret_cast<const uint4 *>(A + (u + v) * 32));
+                    d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                        av, as_v4i(*reinterpret_cast<const uint4 *>(B0 + (u + v) * 32)), d0, 0, 0, 0);
+                    d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                        av, as_v4i(*reinterpret_cast<const uint4 *>(B1 + (u + v) * 32)), d1, 0, 0, 0);
+                }
+                const double s0 = (double)S0[u / GS], s1 = (double)S1[u / GS];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    acc[0][r] = fma((double)d0[r], s0, acc[0][r]);
+                    acc[1][r] = fma((double)d1[r], s1, acc[1][r]);
+                }
             }
-            stage_compute<GS>(lds_a + buf * A_STAGE, lds_b + buf * B_STAGE, arow, R0, R1, hh, shift,
-                              sv0, sv1, acc);
         }
         if (st + 1 < n_stages)
-            lstore(buf ^ 1);
+            LSTORE(buf ^ 1);
         __syncthreads();
     }
+#undef GLOAD
+#undef LSTORE
     if (!active)
         return;
 
