@@ -29,6 +29,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int MT = 128;    // activation rows per tile
+#ifndef MOE_GEMM_NW
+#define MOE_GEMM_NW 16
+#endif
 
 bool use_mfma(const moe_ctx *c, int T)
 {
@@ -344,6 +347,201 @@ void mfma_proj_kernel(ProjArgs a, const int2 *__restrict__ tiles,
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same tile with 16 waves (1024 threads): wave w owns activation block
+// w&3 and one 32-row weight block w>>2, so it holds only 16 fp64 sums per
+// lane and four waves share each SIMD, hiding the epilogue behind the other
+// waves' MFMAs.  GATEUP: weight blocks 0, 1 are gate rows, 2, 3 the matching
+// up rows; after the K loop the up waves hand their sums to the gate waves
+// through LDS (the staging buffers, free by then).
+// ---------------------------------------------------------------------------
+template <bool GATEUP, int GS>
+__global__ __launch_bounds__(1024) void mfma_proj16_kernel(ProjArgs a, const int2 *__restrict__ tiles,
+                                                           const int32_t *__restrict__ n_tiles,
+                                                           int mt_max, int n_blocks,
+                                                           float *__restrict__ out, int ldo)
+{
+    __shared__ __align__(16) uint8_t lds_ab[2 * A_STAGE + 2 * B_STAGE];
+    __shared__ float lds_s[2 * S_STAGE];
+    __shared__ int s_slot[MT], s_row[MT];
+    __shared__ float s_sc[MT];
+    __shared__ int s_tile[8];
+    uint8_t *lds_a = lds_ab, *lds_b = lds_ab + 2 * A_STAGE;
+
+    int nb, mt;
+    block_coords(mt_max, &nb, &mt);
+    if (nb >= n_blocks || mt >= *n_tiles)
+        return;
+    const int2 tl = tiles[mt];
+    const int e = tl.x, m0 = tl.y;
+    const int mc = min(MT, a.rt.cnt[e] - m0);
+    const int tid = threadIdx.x;
+    if (tid < MT) {
+        int slot = -1, row = -1;
+        float sc = 0.0f;
+        if (tid < mc) {
+            slot = a.rt.list[(size_t)e * a.rt.list_stride + m0 + tid];
+            row = a.in_by_token ? slot / a.rt.S : slot;
+            sc = a.s[row];
+        }
+        s_slot[tid] = slot;
+        s_row[tid] = row;
+        s_sc[tid] = sc;
+    }
+    if (tid < 8) {
+        int t;
+        if (GATEUP) {
+            t = (tid < 4) ? 2 * (4 * nb + tid) : 2 * (4 * nb + tid - 4) + 1;
+        } else {
+            const int n = 128 * nb + 16 * tid;
+            t = a.tile_base + (n >> 5) * a.pair_stride + ((n >> 4) & 1) * a.j_stride;
+        }
+        s_tile[tid] = t;
+    }
+    __syncthreads();
+
+    const uint8_t *blob =
+        reinterpret_cast<const uint8_t *>((e == a.ex.E) ? a.ex.shared : a.ex.ptrs[e]);
+    const int K = a.K, KC = K >> 5, n_stages = KC / KB;
+    const uint8_t *qbase = reinterpret_cast<const uint8_t *>(a.q);
+
+    // global -> LDS: activations 1024 pieces of 16 B (1/thread), weight nibbles
+    // 512 pieces (threads < 512, widened to 32 B), scales 128 rows x KB/GS
+    const uint8_t *ga;
+    int la;
+    {
+        const int tok = tid >> 3, seg = tid & 7;
+        const int row = s_row[tok];
+        ga = qbase + (size_t)(row < 0 ? s_row[0] : row) * K + seg * 16;
+        la = tok * A_LD + seg * 16;
+    }
+    const bool b_thread = tid < 512;
+    const uint8_t *gb = nullptr;
+    int lb = 0;
+    if (b_thread) {
+        const int r = tid & 15, kcl = (tid >> 4) & 3, tj = tid >> 6;
+        gb = blob + a.w_off + (size_t)s_tile[tj] * a.tile_w + kcl * 256 + r * 16;
+        lb = (16 * tj + r) * B_LD + kcl * 32;
+    }
+    constexpr int NG = KB / GS;
+    const bool s_thread = tid >= 512 && tid < 512 + 128 * NG;
+    const uint16_t *gs_ = nullptr;
+    int ls_ = 0;
+    if (s_thread) {
+        const int q = tid - 512, row = q / NG, u = q % NG;
+        gs_ = reinterpret_cast<const uint16_t *>(blob + a.s_off + (size_t)s_tile[row >> 4] * a.tile_s) +
+              u * 16 + (row & 15);
+        ls_ = row * KB + u;
+    }
+
+    const int wave = tid >> 6, lane = tid & 63;
+    const int hh = lane >> 5, li = lane & 31;
+    const int mb = wave & 3, wb = wave >> 2;
+    const bool active = __builtin_amdgcn_readfirstlane(32 * mb < mc ? 1 : 0) != 0;
+    const int R = 32 * wb + li;
+    const int arow = 32 * mb + li;
+
+    double acc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        acc[r] = 0.0;
+
+    uint4 ra = {}, rbv = {};
+    uint16_t rs = 0;
+#define GLOAD(stage)                                                              \
+    do {                                                                          \
+        const size_t ko_ = (size_t)(stage) * KB;                                  \
+        ra = *reinterpret_cast<const uint4 *>(ga + ko_ * 32);                     \
+        if (b_thread)                                                             \
+            rbv = *reinterpret_cast<const uint4 *>(gb + ko_ * 256);               \
+        if (s_thread)                                                             \
+            rs = gs_[(size_t)(stage) * NG * 16];                                  \
+    } while (0)
+#define LSTORE(buf)                                                               \
+    do {                                                                          \
+        *reinterpret_cast<uint4 *>(lds_a + (buf) * A_STAGE + la) = ra;            \
+        if (b_thread) {                                                           \
+            *reinterpret_cast<uint4 *>(lds_b + (buf) * B_STAGE + lb) =            \
+                make_uint4((rbv.x << 4) & 0xf0f0f0f0u, (rbv.y << 4) & 0xf0f0f0f0u, \
+                           (rbv.z << 4) & 0xf0f0f0f0u, (rbv.w << 4) & 0xf0f0f0f0u);\
+            *reinterpret_cast<uint4 *>(lds_b + (buf) * B_STAGE + lb + 16) =       \
+                make_uint4(rbv.x & 0xf0f0f0f0u, rbv.y & 0xf0f0f0f0u,              \
+                           rbv.z & 0xf0f0f0f0u, rbv.w & 0xf0f0f0f0u);             \
+        }                                                                         \
+        if (s_thread)                                                             \
+            lds_s[(buf) * S_STAGE + ls_] = f16_to_f32(rs) * 0.0625f;              \
+    } while (0)
+
+    GLOAD(0);
+    LSTORE(0);
+    __syncthreads();
+    for (int st = 0; st < n_stages; ++st) {
+        const int buf = st & 1;
+        if (st + 1 < n_stages)
+            GLOAD(st + 1);
+        if (active) {
+            const uint8_t *A = lds_a + buf * A_STAGE + arow * A_LD + 16 * hh;
+            const uint8_t *B = lds_b + buf * B_STAGE + R * B_LD + 16 * hh;
+            const float *S = lds_s + buf * S_STAGE + R * KB;
+#pragma unroll
+            for (int u = 0; u < KB; u += GS) {
+                const v16i zero = {0};
+                v16i d = zero;
+#pragma unroll
+                for (int v = 0; v < GS; ++v)
+                    d = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                        as_v4i(*reinterpret_cast<const uint4 *>(A + (u + v) * 32)),
+                        as_v4i(*reinterpret_cast<const uint4 *>(B + (u + v) * 32)), d, 0, 0, 0);
+                const double sv = (double)S[u / GS];
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[r] = fma((double)d[r], sv, acc[r]);
+            }
+        }
+        if (st + 1 < n_stages)
+            LSTORE(buf ^ 1);
+        __syncthreads();
+    }
+#undef GLOAD
+#undef LSTORE
+
+    // result register r of lane l: activation row 8(r/4)+4(l/32)+r%4
+    if (GATEUP) {
+        // up waves (wb 2, 3) hand their sums to the gate waves (wb 0, 1)
+        double *xch = reinterpret_cast<double *>(lds_ab);   // [2][4][16][64]
+        if (active && wb >= 2) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                xch[(((wb - 2) * 4 + mb) * 16 + r) * 64 + lane] = acc[r];
+        }
+        __syncthreads();
+        if (!active || wb >= 2)
+            return;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int tok = 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const int slot = s_slot[tok];
+            if (slot < 0)
+                continue;
+            const double sc = (double)s_sc[tok];
+            const double G = acc[r] * sc;
+            const double U = xch[((wb * 4 + mb) * 16 + r) * 64 + lane] * sc;
+            out[(size_t)slot * ldo + 64 * nb + 32 * wb + li] = (float)(G / (1.0 + exp(-G)) * U);
+        }
+    } else {
+        if (!active)
+            return;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int tok = 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const int slot = s_slot[tok];
+            if (slot < 0)
+                continue;
+            out[(size_t)slot * ldo + 128 * nb + 32 * wb + li] = (float)(acc[r] * (double)s_sc[tok]);
+        }
+    }
+}
+
 static int grid_for(int mt_max, int n_blocks)
 {
     long n = (long)mt_max * n_blocks;
@@ -356,10 +554,17 @@ hipError_t launch_gateup_mfma(const ProjArgs &a, const moe_ctx *c, int T, int F,
     const int mt_max = tiles_bound(c, T);
     const int grid = grid_for(mt_max, F / 64);
     const int2 *tl = reinterpret_cast<const int2 *>(c->tiles);
+#if MOE_GEMM_NW == 16
+    if (a.group_shift)
+        launch(mfma_proj16_kernel<true, 2>, grid, 1024, 0, st, a, tl, c->n_tiles, mt_max, F / 64, h, ldh);
+    else
+        launch(mfma_proj16_kernel<true, 1>, grid, 1024, 0, st, a, tl, c->n_tiles, mt_max, F / 64, h, ldh);
+#else
     if (a.group_shift)
         launch(mfma_proj_kernel<true, 2>, grid, 512, 0, st, a, tl, c->n_tiles, mt_max, F / 64, h, ldh);
     else
         launch(mfma_proj_kernel<true, 1>, grid, 512, 0, st, a, tl, c->n_tiles, mt_max, F / 64, h, ldh);
+#endif
     return hipGetLastError();
 }
 
@@ -369,10 +574,17 @@ hipError_t launch_proj_mfma(const ProjArgs &a, const moe_ctx *c, int T, int n_ro
     const int mt_max = (a.ex.E == 0) ? (T + MT - 1) / MT : tiles_bound(c, T);
     const int grid = grid_for(mt_max, n_rows / 128);
     const int2 *tl = reinterpret_cast<const int2 *>(c->tiles);
+#if MOE_GEMM_NW == 16
+    if (a.group_shift)
+        launch(mfma_proj16_kernel<false, 2>, grid, 1024, 0, st, a, tl, c->n_tiles, mt_max, n_rows / 128, a.out, a.ldo);
+    else
+        launch(mfma_proj16_kernel<false, 1>, grid, 1024, 0, st, a, tl, c->n_tiles, mt_max, n_rows / 128, a.out, a.ldo);
+#else
     if (a.group_shift)
         launch(mfma_proj_kernel<false, 2>, grid, 512, 0, st, a, tl, c->n_tiles, mt_max, n_rows / 128, a.out, a.ldo);
     else
         launch(mfma_proj_kernel<false, 1>, grid, 512, 0, st, a, tl, c->n_tiles, mt_max, n_rows / 128, a.out, a.ldo);
+#endif
     return hipGetLastError();
 }
 
