@@ -75,6 +75,40 @@ def test_mfma_project_bit_exact_vs_oracle_and_gemv(g):
     lay.close()
 
 
+@pytest.mark.parametrize("top_field", [21, 22])
+def test_mfma_project_wide_scale_spread_bit_exact(top_field):
+    # One row per part has a scale with exponent field top_field next to the
+    # smallest subnormal (exponent counted as 1): a spread of 20 binades keeps
+    # the kernel's 64-bit integer epilogue at its largest shift, 21 sends the
+    # block to the fp64 epilogue.  Both must equal the oracle bit for bit.
+    H, F, T, g = 512, 256, 70, 32
+    c = Case(14, 1, H, F, 4, 2, 0, g)
+    ex = c.distinct[0]
+    for key, row in (("s_gate", 5), ("s_up", 40), ("s_down", 9)):
+        ex[key] = ex[key].copy()
+        ex[key][row, 0] = top_field << 10
+        ex[key][row, 1] = 0x0001
+        ex[key][row, 2] = 0x8000 | (top_field - 3) << 10      # negative scale
+    lay = c.layer(max_tokens=128, path=abi.PATH_MFMA)
+    r = np.random.default_rng(top_field)
+    for part in range(3):
+        K = F if part == 2 else H
+        N = H if part == 2 else F
+        q = r.integers(-127, 128, size=(T, K)).astype(np.int8)
+        s = r.uniform(1e-3, 1e-1, size=T).astype(np.float32)
+        y = torch.empty((T, N), dtype=torch.float32, device="cuda")
+        abi.moe_debug_project(lay.ctx, lay.blobs[0], part, torch.from_numpy(q).cuda(),
+                              torch.from_numpy(s).cuda(), T, y)
+        _sync()
+        got = y.cpu().numpy()
+        W = ex[("q_gate", "q_up", "q_down")[part]]
+        S = ex[("s_gate", "s_up", "s_down")[part]]
+        for t in range(T):
+            ref = oracle.proj_i4i8(q[t], s[t], W, S, g)
+            assert np.array_equal(got[t].view(np.uint32), ref.view(np.uint32)), (part, t)
+    lay.close()
+
+
 @pytest.mark.parametrize("T,g", [(100, 32), (257, 64)])
 def test_mfma_layer_equals_gemv_layer_and_oracle(T, g):
     c = Case(13, T, 512, 256, 16, 4, 1, g=g, r=2.5)
