@@ -31,15 +31,45 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f)
     return (uint16_t)upper;
 }
 
-__device__ __forceinline__ double shfl_xor_d(double v, int m)
+// The value of lane l ^ S (S a power of two up to 32) of a wave64.  Strides 1
+// and 2 are DPP quad permutes (plain VALU), 4 to 16 ds_swizzle xor masks
+// (within each half-wave, no LDS memory access), 32 a ds_bpermute.
+template <int S>
+__device__ __forceinline__ int xor_lane(int v)
 {
-    return __shfl_xor(v, m, 64);
+    static_assert(S == 1 || S == 2 || S == 4 || S == 8 || S == 16 || S == 32, "lane stride");
+    if constexpr (S == 1)
+        return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+    else if constexpr (S == 2)
+        return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+    else if constexpr (S == 32)
+        return __shfl_xor(v, 32, 64);
+    else
+        return __builtin_amdgcn_ds_swizzle(v, (S << 10) | 0x1F);            // and 31, xor S
+}
+
+template <int S>
+__device__ __forceinline__ float xor_lane_f(float v)
+{
+    return __int_as_float(xor_lane<S>(__float_as_int(v)));
+}
+
+template <int S>
+__device__ __forceinline__ double xor_lane_d(double v)
+{
+    const unsigned long long u = __double_as_longlong(v);
+    const int lo = xor_lane<S>((int)(u & 0xffffffffull)), hi = xor_lane<S>((int)(u >> 32));
+    return __longlong_as_double(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
 }
 
 __device__ __forceinline__ float wave_max(float v)
 {
-    for (int m = 32; m >= 1; m >>= 1)
-        v = fmaxf(v, __shfl_xor(v, m, 64));
+    v = fmaxf(v, xor_lane_f<32>(v));
+    v = fmaxf(v, xor_lane_f<16>(v));
+    v = fmaxf(v, xor_lane_f<8>(v));
+    v = fmaxf(v, xor_lane_f<4>(v));
+    v = fmaxf(v, xor_lane_f<2>(v));
+    v = fmaxf(v, xor_lane_f<1>(v));
     return v;
 }
 
@@ -47,8 +77,12 @@ __device__ __forceinline__ double wave_sum_d(double v)
 {
     // exact when every partial sum is exactly representable (as it is for the
     // group sums of the projections); otherwise a fixed butterfly order
-    for (int m = 32; m >= 1; m >>= 1)
-        v += shfl_xor_d(v, m);
+    v += xor_lane_d<32>(v);
+    v += xor_lane_d<16>(v);
+    v += xor_lane_d<8>(v);
+    v += xor_lane_d<4>(v);
+    v += xor_lane_d<2>(v);
+    v += xor_lane_d<1>(v);
     return v;
 }
 

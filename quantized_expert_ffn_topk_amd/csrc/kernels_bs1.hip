@@ -131,8 +131,8 @@ __device__ __forceinline__ void gateup_pairs(const Bs1Args &a, int ai, int b0, u
         bs1_load<U>(wp, sp_, sstride, j0, wv, sv);
         p = bs1_dot<U>(wv, sv, j0, c4, lq, p);
     }
-    p += shfl_xor_d(p, 16);
-    p += shfl_xor_d(p, 32);
+    p += xor_lane_d<16>(p);
+    p += xor_lane_d<32>(p);
     if (lane < 16)
         sp[pair][half][seg][lane] = p;
     __syncthreads();
@@ -326,11 +326,11 @@ __global__ __launch_bounds__(64 * NW) void down_bs1_kernel(Bs1Args a)
         double p1 = p;
         if (TPW == 1)
             p0 = p;
-        p0 += shfl_xor_d(p0, 16);
-        p0 += shfl_xor_d(p0, 32);
+        p0 += xor_lane_d<16>(p0);
+        p0 += xor_lane_d<32>(p0);
         if (TPW == 2) {
-            p1 += shfl_xor_d(p1, 16);
-            p1 += shfl_xor_d(p1, 32);
+            p1 += xor_lane_d<16>(p1);
+            p1 += xor_lane_d<32>(p1);
         }
         if (lane < 16) {
             float *yg = a.Y + (size_t)ai * a.H + 16 * TPW * pr;

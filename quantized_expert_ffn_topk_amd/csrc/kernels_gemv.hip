@@ -235,8 +235,8 @@ __device__ __forceinline__ void gemv_tile_pair(const ProjArgs &a, const uint8_t 
         }
 #pragma unroll
         for (int m = 0; m < MG; ++m) {
-            p[m] += shfl_xor_d(p[m], 16);
-            p[m] += shfl_xor_d(p[m], 32);
+            p[m] += xor_lane_d<16>(p[m]);
+            p[m] += xor_lane_d<32>(p[m]);
         }
         if (c4 == 0) {
 #pragma unroll

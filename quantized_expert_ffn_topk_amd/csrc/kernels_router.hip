@@ -14,6 +14,21 @@
 
 namespace moe {
 
+// One butterfly step of a wave-wide argmax in the selection order (larger
+// biased score first, the lower expert index on ties), carrying the score.
+template <int S>
+__device__ __forceinline__ void argmax_step(double &bc, int &be, double &bs)
+{
+    const double oc = xor_lane_d<S>(bc);
+    const int oe = xor_lane<S>(be);
+    const double os = xor_lane_d<S>(bs);
+    if (oc > bc || (oc == bc && oe < be)) {
+        bc = oc;
+        be = oe;
+        bs = os;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Per-token int8 quantisation: amax over the row, inv = 127/amax and
 // s = amax/127 in fp32 (correctly rounded), q = clamp(rint(x*inv), -127, 127).
@@ -274,16 +289,12 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
                 }
             }
         }
-        for (int m = 32; m >= 1; m >>= 1) {
-            double oc = __shfl_xor(bc, m, 64);
-            int oe = __shfl_xor(be, m, 64);
-            double os = __shfl_xor(bs, m, 64);
-            if (oc > bc || (oc == bc && oe < be)) {
-                bc = oc;
-                be = oe;
-                bs = os;
-            }
-        }
+        argmax_step<32>(bc, be, bs);
+        argmax_step<16>(bc, be, bs);
+        argmax_step<8>(bc, be, bs);
+        argmax_step<4>(bc, be, bs);
+        argmax_step<2>(bc, be, bs);
+        argmax_step<1>(bc, be, bs);
         if ((be & 63) == lane)
             taken |= 1u << (be >> 6);
         sel_e[i] = be;

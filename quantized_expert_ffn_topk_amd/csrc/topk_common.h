@@ -6,6 +6,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "device_common.h"
+
 #include <climits>
 #include <cstdint>
 
@@ -18,26 +20,48 @@ __device__ __forceinline__ bool sel_before(double ca, int ia, double cb, int ib)
     return ca > cb || (ca == cb && ia < ib);
 }
 
+// One compare-exchange step of the bitonic network over the 64 lanes of a
+// wave: lane pairs at distance STRIDE inside sequences of SIZE lanes.
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ void sort_step(double &c, int &ci)
+{
+    const int lane = threadIdx.x & 63;
+    const double oc = xor_lane_d<STRIDE>(c);
+    const int oi = xor_lane<STRIDE>(ci);
+    const bool lower = (lane & STRIDE) == 0;
+    const bool up = (lane & SIZE) == 0 || SIZE == 64;
+    const bool other_first = sel_before(oc, oi, c, ci);
+    if ((lower == up) ? other_first : !other_first) {
+        c = oc;
+        ci = oi;
+    }
+}
+
 // Bitonic sort of one (c, i) pair per lane across the 64 lanes of a wave, so
 // that lane 0 holds the first in the selection order, lane 1 the second ...
 __device__ __forceinline__ void wave_sort_sel(double &c, int &ci)
 {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const double oc = __shfl_xor(c, stride, 64);
-            const int oi = __shfl_xor(ci, stride, 64);
-            const bool lower = (lane & stride) == 0;
-            const bool up = (lane & size) == 0 || size == 64;
-            const bool other_first = sel_before(oc, oi, c, ci);
-            if ((lower == up) ? other_first : !other_first) {
-                c = oc;
-                ci = oi;
-            }
-        }
-    }
+    sort_step<2, 1>(c, ci);
+    sort_step<4, 2>(c, ci);
+    sort_step<4, 1>(c, ci);
+    sort_step<8, 4>(c, ci);
+    sort_step<8, 2>(c, ci);
+    sort_step<8, 1>(c, ci);
+    sort_step<16, 8>(c, ci);
+    sort_step<16, 4>(c, ci);
+    sort_step<16, 2>(c, ci);
+    sort_step<16, 1>(c, ci);
+    sort_step<32, 16>(c, ci);
+    sort_step<32, 8>(c, ci);
+    sort_step<32, 4>(c, ci);
+    sort_step<32, 2>(c, ci);
+    sort_step<32, 1>(c, ci);
+    sort_step<64, 32>(c, ci);
+    sort_step<64, 16>(c, ci);
+    sort_step<64, 8>(c, ci);
+    sort_step<64, 4>(c, ci);
+    sort_step<64, 2>(c, ci);
+    sort_step<64, 1>(c, ci);
 }
 
 // Top-k of one token for E <= 256, k <= 16, 256 threads.  Thread e < E holds
