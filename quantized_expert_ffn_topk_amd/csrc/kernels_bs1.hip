@@ -27,6 +27,21 @@
 
 namespace moe {
 
+// 16 and 2 bytes read as global-memory loads (generic ones become flat loads,
+// which also count against the LDS wait counter).
+typedef unsigned int gu32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 gload16(const uint4 *p)
+{
+    const gu32x4 v = *(const __attribute__((address_space(1))) gu32x4 *)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint16_t gload2(const uint16_t *p)
+{
+    return *(const __attribute__((address_space(1))) uint16_t *)p;
+}
+
 // One batch of U 16-byte weight loads and their fp16 scales.
 template <int U>
 __device__ __forceinline__ void bs1_load(const uint4 *__restrict__ wp,
@@ -35,8 +50,8 @@ __device__ __forceinline__ void bs1_load(const uint4 *__restrict__ wp,
 {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        wv[u] = wp[(size_t)64 * (j0 + u)];
-        sv[u] = sp[(size_t)sstride * (j0 + u)];
+        wv[u] = gload16(wp + (size_t)64 * (j0 + u));
+        sv[u] = gload2(sp + (size_t)sstride * (j0 + u));
     }
 }
 
