@@ -12,8 +12,9 @@
 // summed; those sums are exact, so the split over lanes does not change the
 // result.  Integer-dot scheme: Colibri guide, table "Points techniques cles".
 //
-//   gateup_bs1_kernel : block (slot, b) = 2 waves, the gate tile 2b and the up
-//                       tile 2b+1 over all of K = hidden; SwiGLU of the 16 rows.
+//   gateup_bs1_kernel : block (slot, b) = the gate tile 2b and the up tile
+//                       2b+1 over all of K = hidden, K split over 2 or 4
+//                       waves per tile; SwiGLU of the 16 rows.
 //   down_bs1_kernel   : block = 16 or 32 output rows, one wave per slot.  Each
 //                       wave requantises its slot's SwiGLU row (same rule as
 //                       the token quantisation) into LDS, projects the 16-row
@@ -394,10 +395,6 @@ bool bs1_supported(int H, int F, int k, int n_shared)
 
 // slots: how many slots from 0 the launch covers (k when the shared expert
 // already ran in the top-k launch, k + n_shared otherwise).
-#ifndef MOE_BS1_GU_KS
-#define MOE_BS1_GU_KS 2
-#endif
-
 template <int KS>
 static void gateup_bs1_u(const Bs1Args &a, dim3 grid, size_t lds, hipStream_t st)
 {
@@ -417,7 +414,12 @@ hipError_t launch_gateup_bs1(const Bs1Args &a, int slots, hipStream_t st)
 {
     const dim3 grid(slots, a.F / 16);
     const size_t lds = (size_t)a.H;
-    gateup_bs1_u<MOE_BS1_GU_KS>(a, grid, lds, st);
+    // K split over 4 waves per tile (12 KB of weights per wave) when the
+    // H/128 chunk batches divide by 4, else over 2 (H is a multiple of 256)
+    if ((a.H >> 7) % 4 == 0)
+        gateup_bs1_u<4>(a, grid, lds, st);
+    else
+        gateup_bs1_u<2>(a, grid, lds, st);
     return hipGetLastError();
 }
 
