@@ -22,6 +22,12 @@
 //                       the slots of its outputs: shared expert first, then
 //                       rank order, in fp64, rounded once.  No cross-block
 //                       hand-off inside a kernel.
+//   down_bs1h_kernel  : the same over half tiles (8 output rows), F = 2048:
+//                       NH half tiles per block so that the grid covers the
+//                       chip's compute units evenly (H/(8 NH) blocks).
+//   topk_bs1h_kernel  : the top-k launch with the shared expert's gate/up
+//                       over half tile pairs (8 gate + 8 up rows per block),
+//                       twice as many blocks as tile pairs.
 #include "device_common.h"
 #include "host_common.h"
 #include "topk_common.h"
@@ -212,6 +218,115 @@ __global__ __launch_bounds__(256) void topk_bs1_kernel(const double *__restrict_
         sel[tid] = s_ptr[s_idx[tid]];
 }
 
+// Gate/up + SwiGLU of half a tile pair (8 gate rows and the matching 8 up
+// rows) for slot ai: block of 8 waves, wave w takes the gate (w < 4) or up
+// tile, K segment w % 4.  Lane l owns row l&7 and chunks kc = 8j + (l>>3) of
+// the segment, NL = H/1024 loads per lane.
+template <int NL>
+__device__ __forceinline__ void gateup_half(const Bs1Args &a, int ai, int q, unsigned char *smem)
+{
+    __shared__ double sp[2][4][8];
+    const uint4 *xsrc = reinterpret_cast<const uint4 *>(a.xq);
+    const int nx = a.H >> 4;                         // <= 512
+    const uint4 xs = xsrc[min((int)threadIdx.x, nx - 1)];
+    const uint8_t *blob = bs1_slot_blob(a, ai);
+    if (!blob)
+        return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int gu = wave >> 2, seg = wave & 3, pp = q >> 1, hf = q & 1;
+    const int r = lane & 7, c8 = lane >> 3, gs = a.group_shift;
+    const int tile = 2 * pp + gu;
+    const int kc0 = seg * NL * 8;
+    const uint4 *wp = reinterpret_cast<const uint4 *>(blob + a.gu_w + (size_t)tile * a.gu_tile_w) +
+                      kc0 * 16 + 8 * hf + r + 16 * c8;
+    const uint16_t *sp_ = reinterpret_cast<const uint16_t *>(blob + a.gu_s + (size_t)tile * a.gu_tile_s) +
+                          ((kc0 >> gs) << 4) + ((c8 >> gs) << 4) + 8 * hf + r;
+    uint4 wv[NL];
+    uint16_t sv[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        wv[j] = gload16(wp + 128 * j);
+        sv[j] = gload2(sp_ + (size_t)(128 >> gs) * j);
+    }
+    if ((int)threadIdx.x < nx)
+        reinterpret_cast<uint4 *>(smem)[threadIdx.x] = xs;
+    __syncthreads();
+    const int8_t *lq = reinterpret_cast<const int8_t *>(smem);
+    double p = 0.0;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        const int c = kc0 + 8 * j + c8;
+        const int4 *qa = reinterpret_cast<const int4 *>(lq + c * 32);
+        const int4 a0 = qa[0], a1 = qa[1];
+        const uint32_t wd[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
+        int acc = 0;
+        acc = sdot4((int)((wd[0] << 4) & 0xf0f0f0f0u), a0.x, acc);
+        acc = sdot4((int)((wd[1] << 4) & 0xf0f0f0f0u), a0.y, acc);
+        acc = sdot4((int)((wd[2] << 4) & 0xf0f0f0f0u), a0.z, acc);
+        acc = sdot4((int)((wd[3] << 4) & 0xf0f0f0f0u), a0.w, acc);
+        acc = sdot4((int)(wd[0] & 0xf0f0f0f0u), a1.x, acc);
+        acc = sdot4((int)(wd[1] & 0xf0f0f0f0u), a1.y, acc);
+        acc = sdot4((int)(wd[2] & 0xf0f0f0f0u), a1.z, acc);
+        acc = sdot4((int)(wd[3] & 0xf0f0f0f0u), a1.w, acc);
+        p = fma((double)acc, (double)f16_to_f32(sv[j]) * 0.0625, p);
+    }
+    p += xor_lane_d<8>(p);
+    p += xor_lane_d<16>(p);
+    p += xor_lane_d<32>(p);
+    if (lane < 8)
+        sp[gu][seg][lane] = p;
+    __syncthreads();
+    if (wave == 0 && lane < 8) {
+        double g = 0.0, u = 0.0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            g += sp[0][t][lane];
+            u += sp[1][t][lane];
+        }
+        const double sa = (double)a.sa[0];
+        const double G = g * sa;
+        const double Uv = u * sa;
+        const double silu = G / (1.0 + exp(-G));
+        a.h[(size_t)ai * a.F + 16 * pp + 8 * hf + lane] = (float)(silu * Uv);
+    }
+}
+
+template <int NL>
+__global__ __launch_bounds__(512) void topk_bs1h_kernel(const double *__restrict__ cs, int E,
+                                                        float r, const void *const *ptrs,
+                                                        int32_t *idx_out, float *w_out,
+                                                        const void **sel, Bs1Args a)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    if (blockIdx.x > 0) {
+        gateup_half<NL>(a, a.k, blockIdx.x - 1, smem);
+        return;
+    }
+    __shared__ double s_s[256], cand_c[64], sel_s[16];
+    __shared__ int cand_i[64], s_idx[16];
+    __shared__ const void *s_ptr[256];
+    const int tid = threadIdx.x;
+    if (tid >= 256) {
+        // the selection runs on waves 0-3; the others pass its three barriers
+        __syncthreads();
+        __syncthreads();
+        __syncthreads();
+        return;
+    }
+    double c = -INFINITY;
+    int ci = INT_MAX;
+    if (tid < E) {
+        c = cs[tid];
+        s_s[tid] = cs[E + tid];
+        ci = tid;
+        if (ptrs)
+            s_ptr[tid] = ptrs[tid];
+    }
+    topk_select_256(c, ci, s_s, a.k, r, idx_out, w_out, s_idx, cand_c, cand_i, sel_s);
+    if (ptrs && tid < a.k)
+        sel[tid] = s_ptr[s_idx[tid]];
+}
+
 // ---------------------------------------------------------------------------
 // Down projection + combine for the TPW 16-row tiles TPW*p, ... of every
 // slot (output rows [16*TPW*p, 16*TPW*(p+1))).  F <= 2048.  Each wave codes its slot's
@@ -377,6 +492,156 @@ __global__ __launch_bounds__(64 * NW) void down_bs1_kernel(Bs1Args a)
     }
 }
 
+// Down projection + combine over half tiles (8 output rows): block pr takes
+// the NH half tiles NH*pr, ..., NH*pr + NH - 1 of every slot (output rows
+// [8*NH*pr, 8*NH*(pr+1))), one wave per slot.  Lane l owns row l&7 of the
+// half tile and chunks kc = 8j + (l>>3), j < 8 (F = 2048): one 16-byte load
+// per lane reads 8 chunks x 128 B of the blob.  A half tile is one batch of
+// 8 loads; two batches are in flight.
+template <int NH>
+__device__ __forceinline__ void dnh_load(const uint8_t *blob, const Bs1Args &a, int hidx, int r,
+                                         int c8, uint4 (&wv)[8], uint16_t (&sv)[8])
+{
+    const int t = hidx >> 1, hf = hidx & 1, gs = a.group_shift;
+    const uint4 *wp = reinterpret_cast<const uint4 *>(blob + a.dn_w + (size_t)t * a.dn_tile_w) +
+                      8 * hf + r + 16 * c8;
+    const uint16_t *sp = reinterpret_cast<const uint16_t *>(blob + a.dn_s + (size_t)t * a.dn_tile_s) +
+                         ((c8 >> gs) << 4) + 8 * hf + r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        wv[j] = gload16(wp + 128 * j);
+        sv[j] = gload2(sp + (size_t)(128 >> gs) * j);
+    }
+}
+
+__device__ __forceinline__ double dnh_dot(const uint4 (&wv)[8], const uint16_t (&sv)[8], int c8,
+                                          const int8_t *__restrict__ lq)
+{
+    double p = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int c = 8 * j + c8;
+        const int4 *qa = reinterpret_cast<const int4 *>(lq + c * 32);
+        const int4 a0 = qa[0], a1 = qa[1];
+        const uint32_t wd[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
+        int acc = 0;
+        acc = sdot4((int)((wd[0] << 4) & 0xf0f0f0f0u), a0.x, acc);
+        acc = sdot4((int)((wd[1] << 4) & 0xf0f0f0f0u), a0.y, acc);
+        acc = sdot4((int)((wd[2] << 4) & 0xf0f0f0f0u), a0.z, acc);
+        acc = sdot4((int)((wd[3] << 4) & 0xf0f0f0f0u), a0.w, acc);
+        acc = sdot4((int)(wd[0] & 0xf0f0f0f0u), a1.x, acc);
+        acc = sdot4((int)(wd[1] & 0xf0f0f0f0u), a1.y, acc);
+        acc = sdot4((int)(wd[2] & 0xf0f0f0f0u), a1.z, acc);
+        acc = sdot4((int)(wd[3] & 0xf0f0f0f0u), a1.w, acc);
+        p = fma((double)acc, (double)f16_to_f32(sv[j]) * 0.0625, p);
+    }
+    return p;
+}
+
+template <int NH>
+__global__ __launch_bounds__(64 * 9) void down_bs1h_kernel(Bs1Args a)
+{
+    extern __shared__ __align__(16) unsigned char smem[];   // S rows of F codes
+    __shared__ float sY[9][8 * NH];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 7, c8 = lane >> 3;
+    const int ai = wave, pr = blockIdx.x;
+    const int F = 2048;
+    int8_t *lq = reinterpret_cast<int8_t *>(smem) + (size_t)ai * F;
+
+    float sc = 0.0f;
+    // the combine's ids and weights, fetched while the weights stream
+    __shared__ float s_w[16];
+    __shared__ int s_e[16];
+    if (threadIdx.x < a.k) {
+        s_e[threadIdx.x] = a.idx[threadIdx.x];
+        s_w[threadIdx.x] = a.w[threadIdx.x];
+    }
+    const float4 *hr = reinterpret_cast<const float4 *>(a.h + (size_t)ai * F);
+    float4 hv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        hv[i] = hr[lane + 64 * i];
+    const uint8_t *blob = bs1_slot_blob(a, ai);
+    if (blob) {
+        uint4 wa[8], wb[8];
+        uint16_t sa[8], sb[8];
+        dnh_load<NH>(blob, a, NH * pr, r, c8, wa, sa);
+        if (NH > 1)
+            dnh_load<NH>(blob, a, NH * pr + 1, r, c8, wb, sb);
+
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(hv[i].x), fabsf(hv[i].y)),
+                                     fmaxf(fabsf(hv[i].z), fabsf(hv[i].w))));
+        amax = wave_max(amax);
+        float inv = 0.0f;
+        if (amax > 0.0f) {
+            inv = 127.0f / amax;
+            sc = amax / 127.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float vv[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w};
+            uint32_t packed = 0u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float q = fminf(fmaxf(rintf(vv[j] * inv), -127.0f), 127.0f);
+                packed |= ((uint32_t)(int)q & 0xffu) << (8 * j);
+            }
+            const int o = 4 * (lane + 64 * i);
+            *reinterpret_cast<uint32_t *>(lq + o) = packed;
+            if (pr == 0)
+                *reinterpret_cast<uint32_t *>(a.qh + (size_t)ai * F + o) = packed;
+        }
+        if (pr == 0 && lane == 0)
+            a.sh[ai] = sc;
+        __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+
+        double ps[NH];
+#pragma unroll
+        for (int i = 0; i < NH; i += 2) {
+            ps[i] = dnh_dot(wa, sa, c8, lq);
+            if (i + 2 < NH)
+                dnh_load<NH>(blob, a, NH * pr + i + 2, r, c8, wa, sa);
+            if (i + 1 < NH) {
+                ps[i + 1] = dnh_dot(wb, sb, c8, lq);
+                if (i + 3 < NH)
+                    dnh_load<NH>(blob, a, NH * pr + i + 3, r, c8, wb, sb);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NH; ++i) {
+            double p = ps[i];
+            p += xor_lane_d<8>(p);
+            p += xor_lane_d<16>(p);
+            p += xor_lane_d<32>(p);
+            if (lane < 8) {
+                const float y = (float)(p * (double)sc);
+                sY[ai][8 * i + r] = y;
+                a.Y[(size_t)ai * a.H + 8 * NH * pr + 8 * i + r] = y;
+            }
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < 8 * NH) {
+        double o = a.n_shared ? (double)sY[a.k][threadIdx.x] : 0.0;
+        for (int i = 0; i < a.k; ++i) {
+            const int ex = s_e[i];
+            if (ex >= 0 && ex < a.ex.E)
+                o = fma((double)s_w[i], (double)sY[i][threadIdx.x], o);
+        }
+        const float f = (float)o;
+        const size_t n = (size_t)8 * NH * pr + threadIdx.x;
+        if (a.out_dtype == MOE_DT_BF16)
+            reinterpret_cast<uint16_t *>(a.out)[n] = f32_to_bf16(f);
+        else
+            reinterpret_cast<float *>(a.out)[n] = f;
+    }
+}
+
 // Loads per lane per batch: the largest of umax, ..., 4, 2 dividing nj = K/128
 // (K is a multiple of 256, so nj is even).
 static int bs1_u(int nj, int umax)
@@ -427,8 +692,19 @@ hipError_t launch_topk_bs1(const double *cs, int E, float r, const void *const *
                            int32_t *idx_out, float *w_out, const void **sel, const Bs1Args &a,
                            hipStream_t st)
 {
-    const int blocks = 1 + (a.n_shared ? a.F / 16 : 0);
     const size_t lds = (size_t)a.H;
+    // shared gate/up over half tile pairs when H/1024 loads per lane fit
+    if (a.n_shared && a.H % 1024 == 0) {
+        const int blocks = 1 + a.F / 8;
+        switch (a.H >> 10) {
+        case 2: launch(topk_bs1h_kernel<2>, blocks, 512, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); return hipGetLastError();
+        case 4: launch(topk_bs1h_kernel<4>, blocks, 512, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); return hipGetLastError();
+        case 6: launch(topk_bs1h_kernel<6>, blocks, 512, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); return hipGetLastError();
+        case 8: launch(topk_bs1h_kernel<8>, blocks, 512, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); return hipGetLastError();
+        default: break;
+        }
+    }
+    const int blocks = 1 + (a.n_shared ? a.F / 16 : 0);
     switch (bs1_u((a.H >> 7) / 2, 16)) {
     case 16: launch(topk_bs1_kernel<16>, blocks, 256, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); break;
     case 12: launch(topk_bs1_kernel<12>, blocks, 256, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); break;
@@ -453,6 +729,19 @@ hipError_t launch_down_bs1(const Bs1Args &a, hipStream_t st)
     const int S = a.k + a.n_shared;
     const dim3 grid(a.H / (16 * TPW));
     const size_t lds = (size_t)S * a.F;
+    // half tiles for F = 2048 and up to 9 slots: NH = H/2048 half tiles per
+    // block (H/(8 NH) blocks, 256 for H = 6144), else one
+    if (S <= 9 && a.F == 2048) {
+        const int nh = (a.H % 2048 == 0) ? a.H / 2048 : 1;
+        const dim3 g(a.H / (8 * nh));
+        switch (nh) {
+        case 1: launch(down_bs1h_kernel<1>, g, 64 * S, lds, st, a); return hipGetLastError();
+        case 2: launch(down_bs1h_kernel<2>, g, 64 * S, lds, st, a); return hipGetLastError();
+        case 3: launch(down_bs1h_kernel<3>, g, 64 * S, lds, st, a); return hipGetLastError();
+        case 4: launch(down_bs1h_kernel<4>, g, 64 * S, lds, st, a); return hipGetLastError();
+        default: break;
+        }
+    }
     // two batches of 2 loads in flight per wave next to the SwiGLU row: for up
     // to 9 slots the block may use 3 waves per SIMD, for up to 16 slots 4
     if (S <= 9)

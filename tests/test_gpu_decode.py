@@ -218,6 +218,37 @@ def test_glm_decode_full_size_sampled():
     lay.close()
 
 
+
+@pytest.mark.parametrize("H,g", [(1536, 32), (2048, 64), (4096, 32), (6144, 64)])
+def test_one_token_half_tile_kernels(H, g):
+    # One token, F 2048, 8 routed + 1 shared expert: the down projection runs
+    # over half tiles (H/2048 of them per block, one when H is not a multiple
+    # of 2048) and, for H a multiple of 1024, the shared expert's gate/up over
+    # half tile pairs inside the top-k launch.  Full outputs, the SwiGLU rows
+    # and their codes of every slot are compared with the oracle.
+    F, E, k = 2048, 16, 8
+    c = Case(40 + H // 512, 1, H, F, E, k, 1, g=g, r=2.5, n_distinct=4)
+    lay = c.layer(max_tokens=1)
+    for step in range(2):
+        c.x = synth.activations(200 + step, 1, H)
+        idx, w, out = lay.forward(lay.x_tensor(c.x))
+        _sync()
+        idx_o, w_o, out_o = c.oracle_layer()
+        _, _, _, _, ch_o = c.oracle_router()
+        check_routing(idx.cpu().numpy(), w.cpu().numpy(), idx_o, w_o, ch_o)
+        check_out(out.cpu().numpy(), out_o)
+        xf = synth.bf16_bits_to_f32(c.x)
+        q_o, s_o = oracle.quant_rows(xf)
+        h = lay.debug_read(3, (1, k + 1, F), torch.float32).cpu().numpy()
+        qh = lay.debug_read(4, (1, k + 1, F), torch.int8).cpu().numpy()
+        idx_g = idx.cpu().numpy()
+        for i in range(k + 1):
+            ex = c.shared if i == k else c.distinct[c.emap[idx_g[0, i]]]
+            ro = oracle.expert(q_o[0], s_o[0], ex, g)
+            assert np.array_equal(h[0, i].view(np.uint32), ro["h"].view(np.uint32)), (step, i)
+            assert np.array_equal(qh[0, i], ro["qh"]), (step, i)
+    lay.close()
+
 def test_graph_replay_matches_eager():
     # Three layer steps captured as one HIP graph, replayed three times with
     # eager work and synchronisations in between; every replay must equal the
