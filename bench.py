@@ -141,7 +141,25 @@ def run_decode(args, lay):
     prof = abi.moe_ctx_profile_read(lay.ctx)
     abi.moe_ctx_profile(lay.ctx, False)
     res["kernels_us"] = {k: 1e3 * v[0] / v[1] for k, v in prof.items() if v[1]}
+    # spread of single steps: events on the launch stream around each eager step
+    n_sp = args.profile_steps
+    if n_sp >= 10:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_sp)]
+        for i in range(n_sp):
+            evs[i][0].record(stream)
+            step(pbase + i)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        res["step_us"] = percentiles([1e3 * a.elapsed_time(b) for a, b in evs])
     return res
+
+
+def percentiles(v):
+    """p10, median and p90 of a list of durations."""
+    v = np.sort(np.asarray(v, dtype=np.float64))
+    return {"p10": float(np.percentile(v, 10)), "p50": float(np.percentile(v, 50)),
+            "p90": float(np.percentile(v, 90)), "n": int(v.size)}
 
 
 def run_prefill(args, lay):
@@ -173,6 +191,14 @@ def run_prefill(args, lay):
         call(i)
     stream.synchronize()
     dt = (time.perf_counter() - t0) / n
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for i in range(n):
+        evs[i][0].record(stream)
+        call(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    call_ms = percentiles([a.elapsed_time(b) for a, b in evs])
     abi.moe_ctx_profile(ctx, True)
     abi.moe_ctx_profile_read(ctx)
     for i in range(n):
@@ -192,6 +218,7 @@ def run_prefill(args, lay):
                     "Zipf(1.1)" % T,
         "tokens_per_s": T / dt,
         "ms_per_call": 1e3 * dt,
+        "ms_per_call_events": call_ms,
         "int8_mfma": {"ops_per_call": ops, "gemm_us": gemm_us,
                       "achieved_TOPS": ops / (gemm_us * 1e-6) / 1e12,
                       "peak_TOPS": INT8_PEAK_TOPS,
@@ -237,6 +264,14 @@ def run_mx(args):
         call(i)
     stream.synchronize()
     dt = (time.perf_counter() - t0) / n
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for i in range(n):
+        evs[i][0].record(stream)
+        call(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    call_ms = percentiles([a.elapsed_time(b) for a, b in evs])
     for i in range(4):                     # experts touched per input
         call(i)
         torch.cuda.synchronize()
@@ -260,6 +295,7 @@ def run_mx(args):
                     "scale 1.0, bias U(-0.01, 0.01)",
         "tokens_per_s": Tm / dt,
         "ms_per_call": 1e3 * dt,
+        "ms_per_call_events": call_ms,
         "experts_touched_per_call": touched,
         "hbm": {"bytes_per_call": layer_bytes,
                 "layer_GBs": layer_bytes / dt / 1e9,
@@ -487,6 +523,7 @@ def main():
             "layer_frac": layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         },
         "kernels_us": {k: round(v, 3) for k, v in res["kernels_us"].items()},
+        "step_us_eager": res.get("step_us"),
         "eager_tokens_per_s": K / res["eager_s"],
         "graph_tokens_per_s": (K / res["graph_s"]) if "graph_s" in res else None,
     }

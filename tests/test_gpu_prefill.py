@@ -128,6 +128,28 @@ def test_mfma_layer_equals_gemv_layer_and_oracle(T, g):
     lay.close()
 
 
+
+@pytest.mark.parametrize("k,n_shared,out_dtype", [(4, 1, "bf16"), (16, 1, "f32"), (8, 0, "f32")])
+def test_many_token_combine(k, n_shared, out_dtype):
+    # The many-token combine (4 outputs per thread, every slot's load issued
+    # first) with k + n_shared from 8 to 17 slots and both output types.
+    T, H, F, E = 90, 512, 256, 32
+    c = Case(60 + k, T, H, F, E, k, n_shared, r=1.5, n_distinct=6)
+    dt = abi.DT_BF16 if out_dtype == "bf16" else abi.DT_F32
+    lay = c.layer(max_tokens=T, path=abi.PATH_MFMA, out_dtype=dt)
+    idx, w, out = lay.forward(lay.x_tensor(c.x))
+    _sync()
+    idx_o, w_o, out_o = c.oracle_layer()
+    _, _, _, _, ch_o = c.oracle_router()
+    check_routing(idx.cpu().numpy(), w.cpu().numpy(), idx_o, w_o, ch_o)
+    if dt == abi.DT_BF16:
+        got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        want = synth.f32_to_bf16_bits(out_o)
+        assert np.mean(got == want) >= 0.999
+    else:
+        check_out(out.cpu().numpy(), out_o)
+    lay.close()
+
 def test_glm_prefill_zipf_full_size_sampled():
     # GLM-shaped prefill: 4096 tokens, hidden 6144, 256 routed + 1 shared,
     # F 2048, top-8, routed scale 2.5, Zipf(1.1)-skewed selection bias.
