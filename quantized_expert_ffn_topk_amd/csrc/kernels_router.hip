@@ -157,13 +157,26 @@ __global__ __launch_bounds__(64 * KS) void router_mfma_kernel(const uint16_t *__
 #pragma unroll
     for (int m = 0; m < MT; ++m)
         acc[m] = f64x4{0.0, 0.0, 0.0, 0.0};
+    // the loads of step k + 32 are issued before step k is summed (the last
+    // step reloads itself, so every load is unconditional and in bounds)
+    float4 w0n = *reinterpret_cast<const float4 *>(wrow);
+    float4 w1n = *reinterpret_cast<const float4 *>(wrow + 4);
+    uint4 xvn[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+        xvn[m] = *reinterpret_cast<const uint4 *>(xrow[m]);
     for (int k = 0; k < KL; k += 32) {
-        const float4 w0 = *reinterpret_cast<const float4 *>(wrow + k);
-        const float4 w1 = *reinterpret_cast<const float4 *>(wrow + k + 4);
+        const float4 w0 = w0n, w1 = w1n;
         uint4 xv[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-            xv[m] = *reinterpret_cast<const uint4 *>(xrow[m] + k);
+            xv[m] = xvn[m];
+        const int kn = min(k + 32, KL - 32);
+        w0n = *reinterpret_cast<const float4 *>(wrow + kn);
+        w1n = *reinterpret_cast<const float4 *>(wrow + kn + 4);
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            xvn[m] = *reinterpret_cast<const uint4 *>(xrow[m] + kn);
         const float wf[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -323,10 +336,59 @@ hipError_t launch_topk(const double *logits, const float *bias, int T, int E, in
 
 // ---------------------------------------------------------------------------
 // Token -> expert permutation.  Block e (e < E) collects, in token order, the
-// slots t*S+i with idx[t,i] == e (ordered compaction by wave ballots); block E
-// (shared expert, when present) takes every token at slot t*S+k.  The last
-// block to finish lists the experts that received rows, in expert order.
+// slots t*S+i with idx[t,i] == e; block E (shared expert, when present) takes
+// every token at slot t*S+k.  The last block to finish lists the experts that
+// received rows, in expert order.
+// Ordered compaction without a barrier per step: wave w owns a contiguous
+// quarter of the T*k entries; a first pass counts its matches (wave ballots),
+// one barrier turns the four counts into offsets, and a second pass writes
+// the matches at their ranks.  Each pass reads batches of 8 entries per lane
+// with the next batch's loads in flight.
 // ---------------------------------------------------------------------------
+constexpr int PERM_U = 8;
+
+// count (WRITE = false) or write (WRITE = true) the matches of e in
+// idx[j_begin, j_end); `base` is the wave's first output rank
+template <bool WRITE>
+__device__ __forceinline__ int permute_pass(const int32_t *__restrict__ idx, int j_begin, int j_end,
+                                            int e, int k, int S, int32_t *__restrict__ mine,
+                                            int list_stride, int base)
+{
+    const int lane = threadIdx.x & 63;
+    const int last = max(j_end - 1, 0);
+    int run = base;
+    int nxt[PERM_U];
+#pragma unroll
+    for (int u = 0; u < PERM_U; ++u)
+        nxt[u] = idx[min(j_begin + 64 * u + lane, last)];
+    for (int j0 = j_begin; j0 < j_end; j0 += 64 * PERM_U) {
+        int cur[PERM_U];
+#pragma unroll
+        for (int u = 0; u < PERM_U; ++u) {
+            cur[u] = nxt[u];
+            nxt[u] = idx[min(j0 + 64 * (PERM_U + u) + lane, last)];
+        }
+#pragma unroll
+        for (int u = 0; u < PERM_U; ++u) {
+            const int j = j0 + 64 * u + lane;
+            const bool m = (j < j_end) && (cur[u] == e);
+            const uint64_t bal = __ballot(m);
+            if (WRITE && m) {
+                const int pos = run + __popcll(bal & ((1ull << lane) - 1ull));
+                // ids repeated within a token (not allowed by the API) could
+                // give an expert more rows than its list holds: extra rows
+                // are dropped
+                if (pos < list_stride) {
+                    const int t = j / k, i = j - t * k;
+                    mine[pos] = t * S + i;
+                }
+            }
+            run += __popcll(bal);
+        }
+    }
+    return run - base;
+}
+
 __global__ __launch_bounds__(256) void permute_kernel(const int32_t *__restrict__ idx, int T,
                                                       int k, int E, int n_shared,
                                                       int32_t *__restrict__ cnt,
@@ -345,26 +407,17 @@ __global__ __launch_bounds__(256) void permute_kernel(const int32_t *__restrict_
     int32_t *mine = list + (size_t)e * list_stride;
     if (e < E) {
         const int N = T * k;
-        for (int j0 = 0; j0 < N; j0 += 256) {
-            int j = j0 + threadIdx.x;
-            bool m = (j < N) && (idx[j] == e);
-            uint64_t bal = __ballot(m);
-            int pre = __popcll(bal & ((1ull << lane) - 1ull));
-            if (lane == 0)
-                wcnt[wave] = __popcll(bal);
-            __syncthreads();
-            int off = total;
-            for (int v = 0; v < wave; ++v)
-                off += wcnt[v];
-            // ids repeated within a token (not allowed by the API) could give
-            // an expert more rows than its list holds: extra rows are dropped
-            if (m && off + pre < list_stride) {
-                int t = j / k, i = j - (j / k) * k;
-                mine[off + pre] = t * S + i;
-            }
-            total += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
-            __syncthreads();
-        }
+        const int Q = (((N + 3) / 4) + 63) & ~63;
+        const int jb = min(wave * Q, N), je = min(jb + Q, N);
+        const int c = permute_pass<false>(idx, jb, je, e, k, S, mine, list_stride, 0);
+        if (lane == 0)
+            wcnt[wave] = c;
+        __syncthreads();
+        int off = 0;
+        for (int v = 0; v < wave; ++v)
+            off += wcnt[v];
+        total = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+        permute_pass<true>(idx, jb, je, e, k, S, mine, list_stride, off);
     } else {
         for (int t = threadIdx.x; t < T; t += 256)
             mine[t] = t * S + k;
