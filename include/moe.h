@@ -262,12 +262,15 @@ moe_status moe_host_free_pinned(void *p);
 const char *moe_last_error(void);
 
 /* ---- kernel timing (measurement) ---------------------------------------------------
- * When on, every hot call on ctx records a HIP event pair around each kernel it
- * enqueues (on the call's stream), waits for the call's last event before
- * returning, and adds each kernel's elapsed time to a per-kind total.  This
- * serialises the host with the GPU once per call; results are unchanged.
- * moe_ctx_profile_read copies the totals (milliseconds) and launch counts for
- * the MOE_PROF_N kinds below and resets them. */
+ * When on, every hot call on ctx has each kernel it enqueues (on the call's
+ * stream) stamped with a HIP event pair taken from the kernel's own dispatch
+ * (hipExtLaunchKernelGGL), from a ring of 256 pairs per kind.  Calls do not wait for the events, so
+ * profiled calls run back to back like unprofiled ones; only when a kind's
+ * ring is full does the next call of that kind wait for its oldest records.
+ * moe_ctx_profile_read waits for every recorded kernel, copies the totals
+ * (milliseconds) and launch counts for the MOE_PROF_N kinds below and resets
+ * them; it returns MOE_E_HIP if an event could not be read.  Results of the
+ * hot calls are unchanged.  Not for use while a stream is being captured. */
 #define MOE_PROF_ROUTER  0    /* router logits */
 #define MOE_PROF_TOPK    1
 #define MOE_PROF_QUANT   2

@@ -250,44 +250,66 @@ ProfSlot &prof_slot()
     return slot;
 }
 
+static hipEvent_t prof_event(moe_ctx *c, int k, int64_t i, int which)
+{
+    return c->prof_ev[((size_t)k * moe_ctx::PROF_RING + (size_t)(i % moe_ctx::PROF_RING)) * 2 + which];
+}
+
+// waits for every recorded launch of kind k and adds up its duration
+static hipError_t prof_drain(moe_ctx *c, int k)
+{
+    for (; c->prof_tail[k] < c->prof_head[k]; ++c->prof_tail[k]) {
+        const int64_t i = c->prof_tail[k];
+        hipError_t e = hipEventSynchronize(prof_event(c, k, i, 1));
+        float ms = 0.0f;
+        if (e == hipSuccess)
+            e = hipEventElapsedTime(&ms, prof_event(c, k, i, 0), prof_event(c, k, i, 1));
+        if (e != hipSuccess) {
+            c->prof_tail[k] = c->prof_head[k];
+            return e;
+        }
+        c->prof_ms[k] += ms;
+        c->prof_cnt[k] += 1;
+    }
+    return hipSuccess;
+}
+
 void prof_begin(moe_ctx *c, int k, hipStream_t st)
 {
     if (!c->prof_on)
         return;
-    (void)hipEventRecord(c->prof_ev[2 * k], st);
+    if (c->prof_head[k] - c->prof_tail[k] >= moe_ctx::PROF_RING) {
+        const hipError_t e = prof_drain(c, k);
+        if (e != hipSuccess && c->prof_err == hipSuccess)
+            c->prof_err = e;
+    }
+    (void)st;
+    const int64_t i = c->prof_head[k];
     ProfSlot &p = prof_slot();
-    p.start = c->prof_ev[2 * k];
-    p.stop = c->prof_ev[2 * k + 1];
+    p.start = prof_event(c, k, i, 0);
+    p.stop = prof_event(c, k, i, 1);
     p.used = false;
 }
 
+// counts the launch if launch() stamped it (a launcher that found nothing to
+// do enqueues no kernel and is not counted)
 void prof_end(moe_ctx *c, int k, hipStream_t st)
 {
+    (void)st;
     if (!c->prof_on)
         return;
     ProfSlot &p = prof_slot();
-    if (!p.used)                 // the launcher did not time the kernel itself
-        (void)hipEventRecord(c->prof_ev[2 * k + 1], st);
+    if (p.used)
+        c->prof_head[k] += 1;
     p = ProfSlot{};
-    c->prof_used[k] = true;
 }
 
 moe_status prof_collect(moe_ctx *c)
 {
-    if (!c->prof_on)
-        return MOE_OK;
-    for (int k = 0; k < MOE_PROF_N; ++k) {
-        if (!c->prof_used[k])
-            continue;
-        hipError_t e = hipEventSynchronize(c->prof_ev[2 * k + 1]);
-        float ms = 0.0f;
-        if (e == hipSuccess)
-            e = hipEventElapsedTime(&ms, c->prof_ev[2 * k], c->prof_ev[2 * k + 1]);
-        if (e != hipSuccess)
-            return hip_fail(e, "profiling events");
-        c->prof_ms[k] += ms;
-        c->prof_cnt[k] += 1;
-        c->prof_used[k] = false;
+    if (c->prof_err != hipSuccess) {
+        const hipError_t e = c->prof_err;
+        c->prof_err = hipSuccess;
+        return hip_fail(e, "profiling events");
     }
     return MOE_OK;
 }
@@ -297,9 +319,10 @@ extern "C" moe_status moe_ctx_profile(moe_ctx *ctx, int32_t on)
 {
     if (!ctx)
         return fail(MOE_E_INVAL, "ctx is NULL");
-    if (on && !ctx->prof_ev[0]) {
-        for (int i = 0; i < 2 * MOE_PROF_N; ++i) {
-            hipError_t e = hipEventCreate(&ctx->prof_ev[i]);
+    if (on && ctx->prof_ev.empty()) {
+        ctx->prof_ev.assign((size_t)2 * MOE_PROF_N * moe_ctx::PROF_RING, nullptr);
+        for (hipEvent_t &ev : ctx->prof_ev) {
+            hipError_t e = hipEventCreate(&ev);
             if (e != hipSuccess)
                 return hip_fail(e, "hipEventCreate");
         }
@@ -312,13 +335,19 @@ extern "C" moe_status moe_ctx_profile_read(moe_ctx *ctx, double *ms, int64_t *co
 {
     if (!ctx || !ms || !counts)
         return fail(MOE_E_INVAL, "NULL argument");
+    hipError_t err = hipSuccess;
+    for (int k = 0; k < MOE_PROF_N; ++k) {
+        const hipError_t e = prof_drain(ctx, k);
+        if (e != hipSuccess && err == hipSuccess)
+            err = e;
+    }
     for (int k = 0; k < MOE_PROF_N; ++k) {
         ms[k] = ctx->prof_ms[k];
         counts[k] = ctx->prof_cnt[k];
         ctx->prof_ms[k] = 0.0;
         ctx->prof_cnt[k] = 0;
     }
-    return MOE_OK;
+    return err != hipSuccess ? hip_fail(err, "profiling events") : MOE_OK;
 }
 
 // Runs `expr` (a launcher returning hipError_t) bracketed by timing events.

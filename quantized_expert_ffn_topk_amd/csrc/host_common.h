@@ -42,10 +42,13 @@ struct moe_ctx {
     // small device constants for single-blob projections
     int32_t *zero1 = nullptr, *one1 = nullptr, *dbg_cnt = nullptr, *ident = nullptr;
     int last_T = 0;
-    // kernel timing
+    // kernel timing: per kind a ring of PROF_RING (start, stop) event pairs;
+    // launches [prof_tail, prof_head) are recorded and not yet added up
+    static constexpr int PROF_RING = 256;
     bool prof_on = false;
-    hipEvent_t prof_ev[2 * MOE_PROF_N] = {};
-    bool prof_used[MOE_PROF_N] = {};
+    std::vector<hipEvent_t> prof_ev;   // [MOE_PROF_N][PROF_RING][2]
+    int64_t prof_head[MOE_PROF_N] = {}, prof_tail[MOE_PROF_N] = {};
+    hipError_t prof_err = hipSuccess;
     double prof_ms[MOE_PROF_N] = {};
     int64_t prof_cnt[MOE_PROF_N] = {};
 };
@@ -57,8 +60,11 @@ moe_status hip_fail(hipError_t e, const char *what);
 moe_status validate_desc(const moe_layer_desc *d);
 moe_status check_device(int device);
 
-// Kernel timing helpers: prof_begin/prof_end bracket one launch of kind `k`;
-// prof_collect waits for the call's events and accumulates.
+// Kernel timing helpers: prof_begin/prof_end bracket one launch of kind `k`
+// with the next event pair of that kind's ring; nothing waits for them until
+// the ring is full or the caller reads the totals (moe_ctx_profile_read), so
+// profiled calls run back to back as unprofiled ones do.  prof_collect
+// reports an error met while draining a full ring.
 void prof_begin(moe_ctx *c, int k, hipStream_t st);
 void prof_end(moe_ctx *c, int k, hipStream_t st);
 moe_status prof_collect(moe_ctx *c);

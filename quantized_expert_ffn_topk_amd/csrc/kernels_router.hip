@@ -233,17 +233,15 @@ hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *Wr
         launch(router_gemv_kernel<4>, grid, 256, 0, st, x, T, H, Wr, E, logits);
         return hipGetLastError();
     }
-    // enough waves to fill the chip: 64-token tiles with 1-2 K slices for many
-    // tokens, 16-token tiles with up to 16 slices for few (H/32 is a multiple
-    // of 8, so 1, 2, 4 and 8 slices of whole 32-input steps always exist)
+    // enough waves to fill the chip: 64-token tiles with 4 K slices for many
+    // tokens (4 waves per SIMD; 1 or 2 slices ran 1.5x slower, 8 slices or
+    // 32-token tiles 1.1-1.2x slower at 4096 tokens), 16-token tiles with up
+    // to 16 slices for few (H/32 is a multiple of 8, so 1, 2, 4 and 8 slices
+    // of whole 32-input steps always exist)
     const int ne = (E + 15) / 16, H32 = H / 32;
     if (T >= 1024) {
         dim3 grid(ne, (T + 63) / 64);
-        const long tiles = (long)grid.x * grid.y;
-        if (tiles >= 2048)
-            launch(router_mfma_kernel<4, 1>, grid, 64, 0, st, x, T, H, Wr, E, logits);
-        else
-            launch(router_mfma_kernel<4, 2>, grid, 128, 0, st, x, T, H, Wr, E, logits);
+        launch(router_mfma_kernel<4, 4>, grid, 256, 0, st, x, T, H, Wr, E, logits);
     } else {
         dim3 grid(ne, (T + 15) / 16);
         const long tiles = (long)grid.x * grid.y;

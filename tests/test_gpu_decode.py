@@ -249,6 +249,43 @@ def test_one_token_half_tile_kernels(H, g):
             assert np.array_equal(qh[0, i], ro["qh"]), (step, i)
     lay.close()
 
+
+def test_kernel_timing_ring_counts_every_launch():
+    # Profiling on: 300 one-token steps back to back (more than the 256 event
+    # pairs per kind, so the ring drains while the steps run); every launch is
+    # counted once with a positive duration, and the outputs equal those of
+    # the same steps without profiling.
+    c = Case(12, 1, 512, 256, 16, 4, 1, r=2.5)
+    lay = c.layer(max_tokens=1)
+    n = 300
+    xs = lay.x_tensor(synth.activations(13, n, 512))
+    outs = [lay._outs(1) for _ in range(2)]
+    ref = []
+    for i in range(n):
+        lay.forward(xs[i:i + 1], outs=outs[0])
+        ref.append(outs[0][2].clone())
+    _sync()
+    abi.moe_ctx_profile(lay.ctx, True)
+    abi.moe_ctx_profile_read(lay.ctx)
+    got = []
+    for i in range(n):
+        lay.forward(xs[i:i + 1], outs=outs[1])
+        got.append(outs[1][2].clone())
+    prof = abi.moe_ctx_profile_read(lay.ctx)
+    abi.moe_ctx_profile(lay.ctx, False)
+    _sync()
+    for a, b in zip(ref, got):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    used = {k: v for k, v in prof.items() if v[1]}
+    assert used, prof
+    for k, (ms, cnt) in used.items():
+        assert cnt == n, (k, cnt)
+        assert ms > 0.0, k
+    # nothing left over for the next read
+    again = abi.moe_ctx_profile_read(lay.ctx)
+    assert all(v[1] == 0 for v in again.values())
+    lay.close()
+
 def test_graph_replay_matches_eager():
     # Three layer steps captured as one HIP graph, replayed three times with
     # eager work and synchronisations in between; every replay must equal the
