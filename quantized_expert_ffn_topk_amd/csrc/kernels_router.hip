@@ -96,26 +96,43 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t *__rest
                                                           int H, const float *__restrict__ Wr,
                                                           int E, double *__restrict__ logits)
 {
+    constexpr int U = 6;                         // 256-input steps whose loads fly together
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int e = blockIdx.x * 4 + wave;
     if (e >= E)
         return;
     const int t0 = blockIdx.y * TB;
     const float *w = Wr + (size_t)e * H;
+    const uint16_t *xr[TB];
+#pragma unroll
+    for (int m = 0; m < TB; ++m)                 // rows past T repeat row T-1 (not stored)
+        xr[m] = x + (size_t)min(t0 + m, T - 1) * H;
     double acc[TB];
 #pragma unroll
     for (int m = 0; m < TB; ++m)
         acc[m] = 0.0;
-    for (int k = lane * 4; k < H; k += 256) {
-        float4 wv = *reinterpret_cast<const float4 *>(w + k);
+    const int nk = H / 256;                      // H is a multiple of 256
+    for (int k0 = 0; k0 < nk; k0 += U) {
+        float4 wv[U];
+        uint2 xv[U][TB];
 #pragma unroll
-        for (int m = 0; m < TB; ++m) {
-            if (t0 + m < T) {
-                uint2 xv = *reinterpret_cast<const uint2 *>(x + (size_t)(t0 + m) * H + k);
-                acc[m] = fma((double)bf16_to_f32(xv.x & 0xffffu), (double)wv.x, acc[m]);
-                acc[m] = fma((double)bf16_to_f32(xv.x >> 16), (double)wv.y, acc[m]);
-                acc[m] = fma((double)bf16_to_f32(xv.y & 0xffffu), (double)wv.z, acc[m]);
-                acc[m] = fma((double)bf16_to_f32(xv.y >> 16), (double)wv.w, acc[m]);
+        for (int u = 0; u < U; ++u) {
+            const int k = 256 * min(k0 + u, nk - 1) + lane * 4;
+            wv[u] = *reinterpret_cast<const float4 *>(w + k);
+#pragma unroll
+            for (int m = 0; m < TB; ++m)
+                xv[u][m] = *reinterpret_cast<const uint2 *>(xr[m] + k);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (k0 + u < nk) {
+#pragma unroll
+                for (int m = 0; m < TB; ++m) {
+                    acc[m] = fma((double)bf16_to_f32(xv[u][m].x & 0xffffu), (double)wv[u].x, acc[m]);
+                    acc[m] = fma((double)bf16_to_f32(xv[u][m].x >> 16), (double)wv[u].y, acc[m]);
+                    acc[m] = fma((double)bf16_to_f32(xv[u][m].y & 0xffffu), (double)wv[u].z, acc[m]);
+                    acc[m] = fma((double)bf16_to_f32(xv[u][m].y >> 16), (double)wv[u].w, acc[m]);
+                }
             }
         }
     }
@@ -323,12 +340,39 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
     }
 }
 
+// Top-k of token t = blockIdx.x for E <= 256: thread e scores expert e, then
+// the bitonic selection of the one-token path (lowest index first on ties).
+__global__ __launch_bounds__(256) void topk256_kernel(const double *__restrict__ logits,
+                                                      const float *__restrict__ bias, int E,
+                                                      int k, float r, int32_t *__restrict__ idx,
+                                                      float *__restrict__ w)
+{
+    __shared__ double s_s[256], cand_c[64], sel_s[16];
+    __shared__ int cand_i[64], s_idx[16];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    double c = -INFINITY;
+    int ci = INT_MAX;
+    if (tid < E) {
+        const double l = logits[(size_t)t * E + tid];
+        const double sv = 1.0 / (1.0 + exp(-l));
+        const double cv = sv + (double)bias[tid];
+        s_s[tid] = sv;
+        c = (cv != cv) ? -INFINITY : cv;
+        ci = tid;
+    }
+    topk_select_256(c, ci, s_s, k, r, idx + (size_t)t * k, w + (size_t)t * k, s_idx, cand_c,
+                    cand_i, sel_s);
+}
+
 hipError_t launch_topk(const double *logits, const float *bias, int T, int E, int k, float r,
                        int32_t *idx, float *w, hipStream_t st)
 {
     if (T <= 0)
         return hipSuccess;
-    launch(topk_kernel, (T + 3) / 4, 256, 0, st, logits, bias, T, E, k, r, idx, w);
+    if (E <= 256 && k <= 16)
+        launch(topk256_kernel, T, 256, 0, st, logits, bias, E, k, r, idx, w);
+    else
+        launch(topk_kernel, (T + 3) / 4, 256, 0, st, logits, bias, T, E, k, r, idx, w);
     return hipGetLastError();
 }
 

@@ -286,6 +286,25 @@ def test_kernel_timing_ring_counts_every_launch():
     assert all(v[1] == 0 for v in again.values())
     lay.close()
 
+
+@pytest.mark.parametrize("F,E,k", [(4096, 16, 4), (512, 32, 16)])
+def test_one_token_gemv_fallback(F, E, k):
+    # One token where the one-token kernels do not apply (F above 2048, or
+    # k + shared above 16 slots): routing, quantisation and lists in one
+    # launch and the GEMV projections with requant and combine fused into
+    # their tails.  Two steps, full outputs and routing against the oracle.
+    c = Case(70 + k, 1, 512, F, E, k, 1, r=2.5, n_distinct=5)
+    lay = c.layer(max_tokens=1)
+    for step in range(2):
+        c.x = synth.activations(300 + step, 1, 512)
+        idx, w, out = lay.forward(lay.x_tensor(c.x))
+        _sync()
+        idx_o, w_o, out_o = c.oracle_layer()
+        _, _, _, _, ch_o = c.oracle_router()
+        check_routing(idx.cpu().numpy(), w.cpu().numpy(), idx_o, w_o, ch_o)
+        check_out(out.cpu().numpy(), out_o)
+    lay.close()
+
 def test_graph_replay_matches_eager():
     # Three layer steps captured as one HIP graph, replayed three times with
     # eager work and synchronisations in between; every replay must equal the
