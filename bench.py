@@ -168,6 +168,39 @@ def percentiles(v):
             "p90": float(np.percentile(v, 90)), "n": int(v.size)}
 
 
+def run_small_batches(args, lay):
+    """Decode steps of 2, 4, 8 and 16 tokens through a second context on the
+    same device blobs: tokens/s and time per step (eager launches)."""
+    import torch
+    from quantized_expert_ffn_topk_amd import abi, synth
+    ctx = abi.moe_ctx_create(0, lay.desc, 16)
+    stream = torch.cuda.Stream()
+    sh = abi.stream_handle(stream)
+    res = {}
+    for T in (2, 4, 8, 16):
+        n = 200
+        xs = lay.x_tensor(synth.activations(20 + T, T * (n + 10), H))
+        idx = torch.empty((T, K_TOP), dtype=torch.int32, device=lay.dev)
+        w = torch.empty((T, K_TOP), dtype=torch.float32, device=lay.dev)
+        out = torch.empty((T, H), dtype=torch.float32, device=lay.dev)
+
+        def call(i):
+            abi.moe_layer_forward(ctx, xs[i * T:(i + 1) * T], T, lay.weights, None, 0, idx, w,
+                                  out, sh)
+
+        for i in range(10):
+            call(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            call(i)
+        stream.synchronize()
+        dt = (time.perf_counter() - t0) / n
+        res[str(T)] = {"tokens_per_s": T / dt, "us_per_step": 1e6 * dt}
+    abi.moe_ctx_destroy(ctx)
+    return res
+
+
 def run_prefill(args, lay):
     """4096-token prefill through a second context on the same device blobs,
     with the Zipf(1.1)-skewed selection bias."""
@@ -441,6 +474,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cpu-steps-max", type=int, default=40)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-small-batches", action="store_true",
+                    help="skip the 2/4/8/16-token decode lines")
     ap.add_argument("--prefill-tokens", type=int, default=4096)
     ap.add_argument("--prefill-calls", type=int, default=5)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -535,6 +570,8 @@ def main():
         "profiled_eager_tokens_per_s": K / res["profiled_s"],
         "graph_tokens_per_s": (K / res["graph_s"]) if "graph_s" in res else None,
     }
+    if not args.no_small_batches:
+        line["decode_small_batches"] = run_small_batches(args, lay)
     if not args.no_prefill:
         line["prefill"] = run_prefill(args, lay)
     if not args.no_stream:
