@@ -57,7 +57,7 @@ __device__ __forceinline__ void bs1_load(const uint4 *__restrict__ wp,
 {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        wv[u] = gload16(wp + (size_t)64 * (j0 + u));
+        wv[u] = load_stream16(wp + (size_t)64 * (j0 + u));
         sv[u] = gload2(sp + (size_t)sstride * (j0 + u));
     }
 }
@@ -509,7 +509,7 @@ __device__ __forceinline__ void dnh_load(const uint8_t *blob, const Bs1Args &a, 
                          ((c8 >> gs) << 4) + 8 * hf + r;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        wv[j] = gload16(wp + 128 * j);
+        wv[j] = load_stream16(wp + 128 * j);
         sv[j] = gload2(sp + (size_t)(128 >> gs) * j);
     }
 }

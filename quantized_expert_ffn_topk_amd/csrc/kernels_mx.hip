@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) void mx_proj_kernel(MxArgs a, const int2 *__re
         uint32_t s8[MX_TPW];
 #pragma unroll
         for (int t = 0; t < MX_TPW; ++t) {
-            w[t] = wt[t][(size_t)c0 * 16];            // 1 KiB per wave: chunks c0..c0+3, 16 rows
+            w[t] = load_stream16(wt[t] + (size_t)c0 * 16);   // 1 KiB per wave: chunks c0..c0+3, 16 rows
             s8[t] = st[t][(size_t)c0 * 16];
         }
         uint4 av[4] = {};
