@@ -415,7 +415,9 @@ __global__ __launch_bounds__(512, 2) void mfma_proj_kernel(ProjArgs a, const int
 #undef GLOAD
 #undef LSTORE
 
-    // result register r of lane l: activation row 8(r/4)+4(l/32)+r%4
+    // result register r of lane l: activation row 8(r/4)+4(l/32)+r%4; the
+    // outputs are read once by the next launch, so they are stored with the
+    // non-temporal hint
     if (GATEUP) {
         // up waves (wb 2, 3) hand their sums to the gate waves (wb 0, 1)
         double *xch = reinterpret_cast<double *>(lds_ab);   // [2][2][16][64]
@@ -436,7 +438,7 @@ __global__ __launch_bounds__(512, 2) void mfma_proj_kernel(ProjArgs a, const int
             const double sc = (double)s_sc[tok];
             const double G_ = acc[r] * sc;
             const double U = xch[((wb * 2 + mb) * 16 + r) * 64 + lane] * sc;
-            out[(size_t)slot * ldo + 64 * nb + 32 * wb + li] = (float)(G_ / (1.0 + exp(-G_)) * U);
+            __builtin_nontemporal_store((float)(G_ / (1.0 + exp(-G_)) * U), out + (size_t)slot * ldo + 64 * nb + 32 * wb + li);
         }
     } else {
         if (!active)
@@ -447,7 +449,7 @@ __global__ __launch_bounds__(512, 2) void mfma_proj_kernel(ProjArgs a, const int
             const int slot = s_slot[tok];
             if (slot < 0)
                 continue;
-            out[(size_t)slot * ldo + NT * nb + 32 * wb + li] = (float)(acc[r] * (double)s_sc[tok]);
+            __builtin_nontemporal_store((float)(acc[r] * (double)s_sc[tok]), out + (size_t)slot * ldo + NT * nb + 32 * wb + li);
         }
     }
 }

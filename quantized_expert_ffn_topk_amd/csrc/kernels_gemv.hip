@@ -517,7 +517,7 @@ hipError_t launch_requant(const float *h, int rows, int F, int8_t *q, float *s, 
 // first sum (S = k + n_shared <= SMAX; slots past S reload slot S-1), so each
 // wave keeps 9 coalesced 256-byte loads in flight instead of one at a time
 // (about 1.7x faster on the 4096-token layer).  Wider vectors per thread
-// (2 or 4 outputs) measured slower.
+// (2 or 4 outputs) measured slower.  Y is read once: non-temporal loads.
 // ---------------------------------------------------------------------------
 template <int SMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ Y,
@@ -535,7 +535,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     float y[SMAX];
 #pragma unroll
     for (int i = 0; i < SMAX; ++i)
-        y[i] = yt[(size_t)min(i, S - 1) * H];
+        y[i] = __builtin_nontemporal_load(yt + (size_t)min(i, S - 1) * H);
     double o = n_shared ? (double)y[k] : 0.0;
 #pragma unroll
     for (int i = 0; i < SMAX; ++i) {
