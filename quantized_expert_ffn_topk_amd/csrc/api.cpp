@@ -449,8 +449,8 @@ static RouteSmallArgs route_small_args(moe_ctx *c, const void *x, int T, const m
     return r;
 }
 
-// Router + top-k.  On the few-token path `extra` (RS_QUANT | RS_LISTS) folds
-// the token quantisation and the routing lists into the same launch.
+// Router + top-k.  On the one-token GEMV path `extra` (RS_QUANT | RS_LISTS)
+// folds the token quantisation and the routing lists into the same launch.
 static moe_status router_enqueue(moe_ctx *c, const void *x, int32_t T, const moe_layer_weights *w,
                                  int32_t *idx, float *gw, hipStream_t st, int extra = 0)
 {
@@ -610,7 +610,6 @@ static moe_status ffn_enqueue(moe_ctx *c, const void *x, int32_t T, const moe_la
     // down -> Y [T*S, H]
     a.q = c->qh;
     a.s = c->sh;
-    a.hsrc = nullptr;
     a.in_by_token = 0;
     a.K = F;
     a.w_off = c->L.dn_w;
@@ -669,10 +668,10 @@ extern "C" moe_status moe_layer_forward(moe_ctx *ctx, const void *x, int32_t T,
     int32_t *idx = idx_out ? idx_out : ctx->idx;
     float *gw = gate_w_out ? gate_w_out : ctx->gw;
     ctx->last_T = T;
-    // few tokens: quantisation (and the routing lists, unless one token needs
-    // none) ride on the router launch.  One token with E <= 256: the router is
-    // two launches, the second also runs the shared expert's gate/up and,
-    // without the cache, picks the ranks' blobs.
+    // one token: quantisation (and, on the GEMV fallback, the routing lists)
+    // ride on the router launch.  One token with E <= 256: the router is two
+    // launches, the second also runs the shared expert's gate/up and, without
+    // the cache, picks the ranks' blobs.
     const bool fused = small_path(ctx, T) && ctx->d.wfmt == MOE_WFMT_INT4;
     const bool bs1 = bs1_path(ctx, T);
     const bool two = bs1 && ctx->d.n_experts <= 256;

@@ -18,10 +18,12 @@
 // before the activation rows are staged in LDS, so the weight stream starts at
 // once.
 //
-// Fused tails (decode, few tokens): the last block to finish an expert's
-// gate/up requantises that expert's SwiGLU rows; the last block to finish an
-// output tile of the down projection combines the experts for that tile.
-// "Last" is decided with a device-scope counter that the last block resets.
+// Fused tails (one token where the one-token kernels do not apply): the last
+// block to finish an expert's gate/up requantises that expert's SwiGLU rows;
+// the last block to finish an output tile of the down projection combines the
+// experts for that tile.  "Last" is decided with a device-scope counter that
+// the last block resets.  From two tokens on, requant and combine run as
+// launches of their own (faster there).
 #include "device_common.h"
 #include "host_common.h"
 
@@ -81,54 +83,6 @@ __device__ __forceinline__ void compute_batch(const uint4 (&wv)[U], const uint16
     }
 }
 
-// Requantises one fp32 row (K <= 4096) into LDS codes with the token
-// quantisation rule; block column 0 also writes codes and scale to global.
-__device__ __forceinline__ void requant_stage(const float *__restrict__ hr, int K, int8_t *lq,
-                                              float *ls, int8_t *gq, float *gs, bool store)
-{
-    __shared__ float red[4];
-    float v[16];
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int i = threadIdx.x * 4 + 1024 * j;
-        if (i < K) {
-            const float4 f = *reinterpret_cast<const float4 *>(hr + i);
-            v[4 * j] = f.x;
-            v[4 * j + 1] = f.y;
-            v[4 * j + 2] = f.z;
-            v[4 * j + 3] = f.w;
-            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
-        }
-    }
-    amax = block_max_256(amax, red);
-    float inv = 0.0f, sc = 0.0f;
-    if (amax > 0.0f) {
-        inv = 127.0f / amax;
-        sc = amax / 127.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int i = threadIdx.x * 4 + 1024 * j;
-        if (i < K) {
-            uint32_t packed = 0u;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const float rr = fminf(fmaxf(rintf(v[4 * j + b] * inv), -127.0f), 127.0f);
-                packed |= ((uint32_t)(int)rr & 0xffu) << (8 * b);
-            }
-            *reinterpret_cast<uint32_t *>(lq + i) = packed;
-            if (store)
-                *reinterpret_cast<uint32_t *>(gq + i) = packed;
-        }
-    }
-    if (threadIdx.x == 0) {
-        *ls = sc;
-        if (store)
-            *gs = sc;
-    }
-}
-
 // Requantises one row of F <= 4096 floats written by other blocks of this
 // kernel (store_dev): all of the thread's loads are issued before any is used.
 __device__ __forceinline__ void requant_row_dev(const float *__restrict__ hr, int F,
@@ -177,18 +131,12 @@ __device__ __forceinline__ void stage_rows(const ProjArgs &a, const int32_t *lst
     for (int m = 0; m < mc; ++m) {
         const int slot = lst[base + m];
         const int row = a.in_by_token ? slot / a.rt.S : slot;
-        if (a.hsrc) {
-            requant_stage(a.hsrc + (size_t)row * K, K, lq + m * K, lsa + m,
-                          const_cast<int8_t *>(a.q) + (size_t)row * K, const_cast<float *>(a.s) + row,
-                          blockIdx.y == 0);
-        } else {
-            const uint4 *src = reinterpret_cast<const uint4 *>(a.q + (size_t)row * K);
-            uint4 *dst = reinterpret_cast<uint4 *>(lq + m * K);
-            for (int i = threadIdx.x; i < K / 16; i += 256)
-                dst[i] = src[i];
-            if (threadIdx.x == 0)
-                lsa[m] = a.s[row];
-        }
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.q + (size_t)row * K);
+        uint4 *dst = reinterpret_cast<uint4 *>(lq + m * K);
+        for (int i = threadIdx.x; i < K / 16; i += 256)
+            dst[i] = src[i];
+        if (threadIdx.x == 0)
+            lsa[m] = a.s[row];
         if (threadIdx.x == 0)
             lslot[m] = slot;
     }

@@ -88,7 +88,7 @@ hipError_t launch_quant_tokens(const uint16_t *x, int T, int H, int8_t *q, float
 // ---------------------------------------------------------------------------
 // Router logits l[t,e] = sum_k x[t,k]*Wr[e,k] in fp64 (bf16 x fp32 products
 // are exact in fp64).
-// Few tokens: one wave per expert streams its router row with 16-byte loads
+// 2-16 tokens: one wave per expert streams its router row with 16-byte loads
 // for up to TB tokens.  Many tokens: the fp64 MFMA below.
 // ---------------------------------------------------------------------------
 template <int TB>

@@ -84,10 +84,6 @@ struct ProjArgs {
     // activation rows (int8 codes, fp32 scale)
     const int8_t *q;
     const float *s;
-    // few-token down projection: stage rows by requantising these fp32 rows
-    // (SwiGLU outputs) instead of reading q/s; block column 0 also stores the
-    // codes and scales to q/s
-    const float *hsrc;
     int in_by_token;           // 1: input row = slot / S, 0: input row = slot
     int K;
     int group_shift;           // log2(group / 32)
@@ -99,7 +95,7 @@ struct ProjArgs {
     int ldo;
 };
 
-// Fused tails of the few-token GEMV path: requantisation of the SwiGLU rows
+// Fused tails of the one-token GEMV path: requantisation of the SwiGLU rows
 // (gate/up) and the combine (down); ctr is a zeroed device counter array.
 struct TailArgs {
     int8_t *qh;
