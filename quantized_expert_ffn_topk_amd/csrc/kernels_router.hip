@@ -14,21 +14,6 @@
 
 namespace moe {
 
-// One butterfly step of a wave-wide argmax in the selection order (larger
-// biased score first, the lower expert index on ties), carrying the score.
-template <int S>
-__device__ __forceinline__ void argmax_step(double &bc, int &be, double &bs)
-{
-    const double oc = xor_lane_d<S>(bc);
-    const int oe = xor_lane<S>(be);
-    const double os = xor_lane_d<S>(bs);
-    if (oc > bc || (oc == bc && oe < be)) {
-        bc = oc;
-        be = oe;
-        bs = os;
-    }
-}
-
 // ---------------------------------------------------------------------------
 // Per-token int8 quantisation: amax over the row, inv = 127/amax and
 // s = amax/127 in fp32 (correctly rounded), q = clamp(rint(x*inv), -127, 127).
@@ -270,85 +255,16 @@ hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *Wr
     return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Top-k per token, one wave per token.  Score s = 1/(1+exp(-l)), choice
-// c = s + bias (fp64).  k rounds of a wave-wide argmax over (c desc, index
-// asc); NaN choices rank as -inf.  Gate weights s/sum(s)*r summed in rank
-// order.  E <= 1024 (16 candidates per lane).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ logits,
-                                                   const float *__restrict__ bias, int T, int E,
-                                                   int k, float r, int32_t *__restrict__ idx,
-                                                   float *__restrict__ w)
-{
-    constexpr int PL = 16;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + wave;
-    if (t >= T)
-        return;
-    double c[PL], s[PL];
-#pragma unroll
-    for (int j = 0; j < PL; ++j) {
-        int e = lane + 64 * j;
-        if (e < E) {
-            double l = logits[(size_t)t * E + e];
-            s[j] = 1.0 / (1.0 + exp(-l));
-            double cv = s[j] + (double)bias[e];
-            c[j] = (cv != cv) ? -INFINITY : cv;
-        } else {
-            s[j] = 0.0;
-            c[j] = -INFINITY;
-        }
-    }
-    uint32_t taken = 0u;
-    int sel_e[16];
-    double sel_s[16];
-    for (int i = 0; i < k; ++i) {
-        double bc = -INFINITY, bs = 0.0;
-        int be = INT_MAX;
-#pragma unroll
-        for (int j = 0; j < PL; ++j) {
-            int e = lane + 64 * j;
-            if (e < E && !((taken >> j) & 1u)) {
-                if (c[j] > bc || (c[j] == bc && e < be)) {
-                    bc = c[j];
-                    be = e;
-                    bs = s[j];
-                }
-            }
-        }
-        argmax_step<32>(bc, be, bs);
-        argmax_step<16>(bc, be, bs);
-        argmax_step<8>(bc, be, bs);
-        argmax_step<4>(bc, be, bs);
-        argmax_step<2>(bc, be, bs);
-        argmax_step<1>(bc, be, bs);
-        if ((be & 63) == lane)
-            taken |= 1u << (be >> 6);
-        sel_e[i] = be;
-        sel_s[i] = bs;
-    }
-    if (lane == 0) {
-        double den = 0.0;
-        for (int i = 0; i < k; ++i)
-            den += sel_s[i];
-        for (int i = 0; i < k; ++i) {
-            double wi = (den > 0.0) ? (sel_s[i] / den) * (double)r : 0.0;
-            idx[(size_t)t * k + i] = sel_e[i];
-            w[(size_t)t * k + i] = (float)wi;
-        }
-    }
-}
-
-// Top-k of token t = blockIdx.x for E <= 256: thread e scores expert e, then
+// Top-k of token t = blockIdx.x for E <= 64*NW: thread e scores expert e, then
 // the bitonic selection of the one-token path (lowest index first on ties).
-__global__ __launch_bounds__(256) void topk256_kernel(const double *__restrict__ logits,
-                                                      const float *__restrict__ bias, int E,
-                                                      int k, float r, int32_t *__restrict__ idx,
-                                                      float *__restrict__ w)
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void topk_block_kernel(const double *__restrict__ logits,
+                                                             const float *__restrict__ bias, int E,
+                                                             int k, float r, int32_t *__restrict__ idx,
+                                                             float *__restrict__ w)
 {
-    __shared__ double s_s[256], cand_c[64], sel_s[16];
-    __shared__ int cand_i[64], s_idx[16];
+    __shared__ double s_s[64 * NW], cand_c[16 * NW], sel_s[16];
+    __shared__ int cand_i[16 * NW], s_idx[16];
     const int t = blockIdx.x, tid = threadIdx.x;
     double c = -INFINITY;
     int ci = INT_MAX;
@@ -360,8 +276,8 @@ __global__ __launch_bounds__(256) void topk256_kernel(const double *__restrict__
         c = (cv != cv) ? -INFINITY : cv;
         ci = tid;
     }
-    topk_select_256(c, ci, s_s, k, r, idx + (size_t)t * k, w + (size_t)t * k, s_idx, cand_c,
-                    cand_i, sel_s);
+    topk_select_waves<NW>(c, ci, s_s, k, r, idx + (size_t)t * k, w + (size_t)t * k, s_idx, cand_c,
+                          cand_i, sel_s);
 }
 
 hipError_t launch_topk(const double *logits, const float *bias, int T, int E, int k, float r,
@@ -369,10 +285,13 @@ hipError_t launch_topk(const double *logits, const float *bias, int T, int E, in
 {
     if (T <= 0)
         return hipSuccess;
-    if (E <= 256 && k <= 16)
-        launch(topk256_kernel, T, 256, 0, st, logits, bias, E, k, r, idx, w);
+    // E <= 1024 and k <= 16 (checked at context creation)
+    if (E <= 256)
+        launch(topk_block_kernel<4>, T, 256, 0, st, logits, bias, E, k, r, idx, w);
+    else if (E <= 512)
+        launch(topk_block_kernel<8>, T, 512, 0, st, logits, bias, E, k, r, idx, w);
     else
-        launch(topk_kernel, (T + 3) / 4, 256, 0, st, logits, bias, T, E, k, r, idx, w);
+        launch(topk_block_kernel<16>, T, 1024, 0, st, logits, bias, E, k, r, idx, w);
     return hipGetLastError();
 }
 

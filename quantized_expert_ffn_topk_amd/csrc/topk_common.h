@@ -64,16 +64,19 @@ __device__ __forceinline__ void wave_sort_sel(double &c, int &ci)
     sort_step<64, 1>(c, ci);
 }
 
-// Top-k of one token for E <= 256, k <= 16, 256 threads.  Thread e < E holds
-// the biased score c of expert e (NaN already mapped to -inf) and has put its
-// sigmoid score in s_s[e]; other threads hold (-inf, INT_MAX).  Each wave
-// sorts its 64 candidates, wave 0 sorts the first 16 of every wave again.
-// Writes the ranks' ids (s_idx too) and weights w_i = s_i / sum(s) * r, the
-// sum taken in rank order in fp64.
-__device__ __forceinline__ void topk_select_256(double c, int ci, const double *s_s, int k,
-                                                float r, int32_t *__restrict__ idx_out,
-                                                float *__restrict__ w_out, int32_t *s_idx,
-                                                double *cand_c, int *cand_i, double *sel_s)
+// Top-k of one token for E <= 64*NW (NW = 4, 8 or 16 waves), k <= 16.
+// Thread e < E holds the biased score c of expert e (NaN already mapped to
+// -inf) and has put its sigmoid score in s_s[e]; other threads hold (-inf,
+// INT_MAX).  Each wave sorts its 64 candidates and keeps the first 16; while
+// more than 64 remain, waves sort them again 64 at a time; wave 0 sorts the
+// last at most 64.  The order is total, so the grouping does not change the
+// result.  Writes the ranks' ids (s_idx too) and weights w_i = s_i / sum(s) *
+// r, the sum taken in rank order in fp64.  cand_c/cand_i hold 16*NW entries.
+template <int NW>
+__device__ __forceinline__ void topk_select_waves(double c, int ci, const double *s_s, int k,
+                                                  float r, int32_t *__restrict__ idx_out,
+                                                  float *__restrict__ w_out, int32_t *s_idx,
+                                                  double *cand_c, int *cand_i, double *sel_s)
 {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     wave_sort_sel(c, ci);                            // s_s is read after the next barrier
@@ -82,9 +85,27 @@ __device__ __forceinline__ void topk_select_256(double c, int ci, const double *
         cand_i[wave * 16 + lane] = ci;
     }
     __syncthreads();
+    constexpr int N1 = 16 * NW;                      // 64, 128 or 256 candidates
+    constexpr int N2 = N1 > 64 ? N1 / 4 : N1;        // after one more round: <= 64
+    if (N1 > 64) {
+        constexpr int nw = N1 / 64;
+        double cc = -INFINITY;
+        int cci = INT_MAX;
+        if (wave < nw) {
+            cc = cand_c[64 * wave + lane];
+            cci = cand_i[64 * wave + lane];
+            wave_sort_sel(cc, cci);
+        }
+        __syncthreads();
+        if (wave < nw && lane < 16) {
+            cand_c[16 * wave + lane] = cc;
+            cand_i[16 * wave + lane] = cci;
+        }
+        __syncthreads();
+    }
     if (wave == 0) {
-        c = cand_c[lane];
-        ci = cand_i[lane];
+        c = lane < N2 ? cand_c[lane] : -INFINITY;
+        ci = lane < N2 ? cand_i[lane] : INT_MAX;
         wave_sort_sel(c, ci);
         if (lane < k) {
             s_idx[lane] = ci;
@@ -101,6 +122,15 @@ __device__ __forceinline__ void topk_select_256(double c, int ci, const double *
         w_out[tid] = (float)wi;
     }
     __syncthreads();
+}
+
+// E <= 256 on 256 threads (three barriers).
+__device__ __forceinline__ void topk_select_256(double c, int ci, const double *s_s, int k,
+                                                float r, int32_t *__restrict__ idx_out,
+                                                float *__restrict__ w_out, int32_t *s_idx,
+                                                double *cand_c, int *cand_i, double *sel_s)
+{
+    topk_select_waves<4>(c, ci, s_s, k, r, idx_out, w_out, s_idx, cand_c, cand_i, sel_s);
 }
 
 }  // namespace moe

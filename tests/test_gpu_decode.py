@@ -337,9 +337,12 @@ def test_graph_replay_matches_eager():
     lay.close()
 
 
-@pytest.mark.parametrize("T,E", [(17, 40), (100, 64), (300, 256), (1100, 48)])
+@pytest.mark.parametrize("T,E", [(17, 40), (100, 64), (300, 256), (1100, 48), (5, 300), (40, 513),
+                                 (20, 1024)])
 def test_router_logits_many_tokens(T, E):
-    # the fp64 MFMA router (more than 16 tokens), E not a multiple of 16 included
+    # the router GEMV (up to 16 tokens) and the fp64 MFMA router (more), E not
+    # a multiple of 16 included, and the block top-k with 4, 8 and 16 waves
+    # (E up to 256, 512 and 1024)
     c = Case(30 + T, T, 1024, 256, E, 6, 0, n_distinct=1)
     lay = c.layer()
     idx, w = lay.router(lay.x_tensor(c.x))
