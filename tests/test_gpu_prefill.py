@@ -150,6 +150,57 @@ def test_many_token_combine(k, n_shared, out_dtype):
         check_out(out.cpu().numpy(), out_o)
     lay.close()
 
+
+def test_mfma_layer_many_experts():
+    # 600 routed experts + shared on the MFMA path: the tile list and the
+    # block top-k with 16 waves; full outputs against the oracle
+    T, H, F, E, k = 130, 512, 256, 600, 8
+    c = Case(90, T, H, F, E, k, 1, r=2.5, n_distinct=7)
+    lay = c.layer(max_tokens=T, path=abi.PATH_MFMA)
+    idx, w, out = lay.forward(lay.x_tensor(c.x))
+    _sync()
+    idx_o, w_o, out_o = c.oracle_layer()
+    _, _, _, _, ch_o = c.oracle_router()
+    check_routing(idx.cpu().numpy(), w.cpu().numpy(), idx_o, w_o, ch_o)
+    check_out(out.cpu().numpy(), out_o)
+    lay.close()
+
+
+@pytest.mark.parametrize("T,path", [(100, abi.PATH_MFMA), (5, abi.PATH_AUTO)])
+def test_graph_replay_matches_eager_many_tokens(T, path):
+    # Two layer calls (MFMA path at 100 tokens; router GEMV, block top-k,
+    # one-block permutation and GEMV projections at 5) captured as one HIP
+    # graph and replayed three times with eager work and synchronisations in
+    # between; every replay equals the eager results bit for bit.
+    H, F, E, k = 512, 256, 32, 4
+    c = Case(91 + T, T, H, F, E, k, 1, r=2.5, n_distinct=5)
+    lay = c.layer(max_tokens=T, path=path)
+    xs = [lay.x_tensor(synth.activations(95 + i, T, H)) for i in range(2)]
+    s = torch.cuda.Stream()
+    outs = [lay._outs(T) for _ in range(2)]
+    with torch.cuda.stream(s):
+        for i in range(2):
+            lay.forward(xs[i], stream=s, outs=outs[i])
+    s.synchronize()
+    eager = [(o[0].clone(), o[2].clone()) for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(2):
+            lay.forward(xs[i], stream=s, outs=outs[i])
+    for rep in range(3):
+        for o in outs:
+            o[2].fill_(float("nan"))
+            o[0].fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i][0], eager[i][0]), (rep, i)
+            assert torch.equal(outs[i][2].view(torch.int32), eager[i][1].view(torch.int32)), (rep, i)
+        lay.forward(xs[rep % 2])
+        torch.cuda.synchronize()
+    del g
+    lay.close()
+
 def test_glm_prefill_zipf_full_size_sampled():
     # GLM-shaped prefill: 4096 tokens, hidden 6144, 256 routed + 1 shared,
     # F 2048, top-8, routed scale 2.5, Zipf(1.1)-skewed selection bias.
