@@ -450,7 +450,8 @@ static RouteSmallArgs route_small_args(moe_ctx *c, const void *x, int T, const m
 }
 
 // Router + top-k.  On the one-token GEMV path `extra` (RS_QUANT | RS_LISTS)
-// folds the token quantisation and the routing lists into the same launch.
+// folds the token quantisation and the routing lists into the same launch;
+// otherwise RS_QUANT has the top-k launch quantise the tokens (hidden <= 8192).
 static moe_status router_enqueue(moe_ctx *c, const void *x, int32_t T, const moe_layer_weights *w,
                                  int32_t *idx, float *gw, hipStream_t st, int extra = 0)
 {
@@ -465,9 +466,11 @@ static moe_status router_enqueue(moe_ctx *c, const void *x, int32_t T, const moe
     LAUNCH(MOE_PROF_ROUTER, "router logits launch",
            launch_router_logits(static_cast<const uint16_t *>(x), T, d.hidden, w->router_w,
                                 d.n_experts, c->logits, st));
+    const bool q = (extra & RS_QUANT) != 0;
     LAUNCH(MOE_PROF_TOPK, "top-k launch",
            launch_topk(c->logits, w->router_bias, T, d.n_experts, d.top_k, d.routed_scale, idx,
-                       gw, st));
+                       gw, st, q ? static_cast<const uint16_t *>(x) : nullptr, d.hidden,
+                       q ? c->xq : nullptr, q ? c->sa : nullptr));
     return MOE_OK;
 }
 
@@ -552,8 +555,9 @@ static moe_status ffn_enqueue(moe_ctx *c, const void *x, int32_t T, const moe_la
                                                    const_cast<float *>(gw), RS_QUANT | RS_LISTS),
                                   st));
     } else if (!small) {
-        LAUNCH(MOE_PROF_QUANT, "quant launch",
-               launch_quant_tokens(static_cast<const uint16_t *>(x), T, H, c->xq, c->sa, st));
+        if (!prepped)
+            LAUNCH(MOE_PROF_QUANT, "quant launch",
+                   launch_quant_tokens(static_cast<const uint16_t *>(x), T, H, c->xq, c->sa, st));
         LAUNCH(MOE_PROF_PERMUTE, "permute launch",
                launch_permute(idx, T, k, E, d.n_shared, c->cnt, c->list, c->max_tokens, c->active,
                               c->n_active, c->done, st));
@@ -676,11 +680,13 @@ extern "C" moe_status moe_layer_forward(moe_ctx *ctx, const void *x, int32_t T,
     const bool bs1 = bs1_path(ctx, T);
     const bool two = bs1 && ctx->d.n_experts <= 256;
     const bool sel = two && !cache && w->expert_ptrs;
+    // more tokens: the top-k launch quantises them
+    const bool rq = !bs1 && !fused && ctx->d.wfmt == MOE_WFMT_INT4 && ctx->d.hidden <= 8192;
     if (two)
         s = router_bs1_enqueue(ctx, x, w, idx, gw, sel, st);
     else
         s = router_enqueue(ctx, x, T, w, idx, gw, st,
-                           bs1 ? RS_QUANT : fused ? (RS_QUANT | RS_LISTS) : 0);
+                           (bs1 || rq) ? RS_QUANT : fused ? (RS_QUANT | RS_LISTS) : 0);
     if (s)
         return s;
     const void *const *ptrs = w->expert_ptrs;
@@ -691,7 +697,7 @@ extern "C" moe_status moe_layer_forward(moe_ctx *ctx, const void *x, int32_t T,
         if (s)
             return s;
     }
-    s = ffn_enqueue(ctx, x, T, w, ptrs, idx, gw, out, st, fused, sel, two && ctx->d.n_shared);
+    s = ffn_enqueue(ctx, x, T, w, ptrs, idx, gw, out, st, fused || rq, sel, two && ctx->d.n_shared);
     if (s)
         return s;
     return prof_collect(ctx);

@@ -257,15 +257,30 @@ hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *Wr
 
 // Top-k of token t = blockIdx.x for E <= 64*NW: thread e scores expert e, then
 // the bitonic selection of the one-token path (lowest index first on ties).
+// With xq set the block also quantises token t (the rule of
+// quant_tokens_kernel), its row loads issued before the selection.
 template <int NW>
 __global__ __launch_bounds__(64 * NW) void topk_block_kernel(const double *__restrict__ logits,
                                                              const float *__restrict__ bias, int E,
                                                              int k, float r, int32_t *__restrict__ idx,
-                                                             float *__restrict__ w)
+                                                             float *__restrict__ w,
+                                                             const uint16_t *__restrict__ x, int H,
+                                                             int8_t *__restrict__ xq,
+                                                             float *__restrict__ sa)
 {
+    constexpr int NT = 64 * NW;
+    constexpr int XL = 8192 / (8 * NT);          // 16-byte pieces per thread, H <= 8192
     __shared__ double s_s[64 * NW], cand_c[16 * NW], sel_s[16];
     __shared__ int cand_i[16 * NW], s_idx[16];
+    __shared__ float s_am[NW];
     const int t = blockIdx.x, tid = threadIdx.x;
+    uint4 xv[XL];
+    if (xq) {
+        const uint4 *xr = reinterpret_cast<const uint4 *>(x + (size_t)t * H);
+#pragma unroll
+        for (int i = 0; i < XL; ++i)               // clamped: every load in bounds
+            xv[i] = xr[min(tid + NT * i, H / 8 - 1)];
+    }
     double c = -INFINITY;
     int ci = INT_MAX;
     if (tid < E) {
@@ -278,20 +293,63 @@ __global__ __launch_bounds__(64 * NW) void topk_block_kernel(const double *__res
     }
     topk_select_waves<NW>(c, ci, s_s, k, r, idx + (size_t)t * k, w + (size_t)t * k, s_idx, cand_c,
                           cand_i, sel_s);
+    if (!xq)
+        return;
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+        if (8 * (tid + NT * i) < H) {
+            const uint32_t wd[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                amax = fmaxf(amax, fmaxf(fabsf(bf16_to_f32(wd[j] & 0xffffu)), fabsf(bf16_to_f32(wd[j] >> 16))));
+        }
+    }
+    amax = wave_max(amax);
+    if ((tid & 63) == 0)
+        s_am[tid >> 6] = amax;
+    __syncthreads();
+    amax = s_am[0];
+#pragma unroll
+    for (int v = 1; v < NW; ++v)
+        amax = fmaxf(amax, s_am[v]);
+    float inv = 0.0f, sc = 0.0f;
+    if (amax > 0.0f) {
+        inv = 127.0f / amax;
+        sc = amax / 127.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+        const int p = tid + NT * i;
+        if (8 * p < H) {
+            const uint32_t wd[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+            uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float xf = bf16_to_f32((j & 1) ? (wd[j >> 1] >> 16) : (wd[j >> 1] & 0xffffu));
+                const float q = fminf(fmaxf(rintf(xf * inv), -127.0f), 127.0f);
+                packed[j >> 2] |= ((uint32_t)(int)q & 0xffu) << (8 * (j & 3));
+            }
+            *reinterpret_cast<uint2 *>(xq + (size_t)t * H + 8 * p) = make_uint2(packed[0], packed[1]);
+        }
+    }
+    if (tid == 0)
+        sa[t] = sc;
 }
 
 hipError_t launch_topk(const double *logits, const float *bias, int T, int E, int k, float r,
-                       int32_t *idx, float *w, hipStream_t st)
+                       int32_t *idx, float *w, hipStream_t st, const uint16_t *x, int H,
+                       int8_t *xq, float *sa)
 {
     if (T <= 0)
         return hipSuccess;
     // E <= 1024 and k <= 16 (checked at context creation)
     if (E <= 256)
-        launch(topk_block_kernel<4>, T, 256, 0, st, logits, bias, E, k, r, idx, w);
+        launch(topk_block_kernel<4>, T, 256, 0, st, logits, bias, E, k, r, idx, w, x, H, xq, sa);
     else if (E <= 512)
-        launch(topk_block_kernel<8>, T, 512, 0, st, logits, bias, E, k, r, idx, w);
+        launch(topk_block_kernel<8>, T, 512, 0, st, logits, bias, E, k, r, idx, w, x, H, xq, sa);
     else
-        launch(topk_block_kernel<16>, T, 1024, 0, st, logits, bias, E, k, r, idx, w);
+        launch(topk_block_kernel<16>, T, 1024, 0, st, logits, bias, E, k, r, idx, w, x, H, xq, sa);
     return hipGetLastError();
 }
 
