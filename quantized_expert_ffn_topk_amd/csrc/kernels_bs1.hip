@@ -730,15 +730,17 @@ hipError_t launch_down_bs1(const Bs1Args &a, hipStream_t st)
     const dim3 grid(a.H / (16 * TPW));
     const size_t lds = (size_t)S * a.F;
     // half tiles for F = 2048 and up to 9 slots: NH = H/2048 half tiles per
-    // block (H/(8 NH) blocks, 256 for H = 6144), else one
+    // block (H/(8 NH) blocks, 256 for H = 6144), else one; H = 8192 takes two
+    // over 512 blocks (four would hold more load registers than fit: spills)
     if (S <= 9 && a.F == 2048) {
-        const int nh = (a.H % 2048 == 0) ? a.H / 2048 : 1;
+        int nh = (a.H % 2048 == 0) ? a.H / 2048 : 1;
+        if (nh > 3)
+            nh = (nh % 2 == 0) ? 2 : 1;
         const dim3 g(a.H / (8 * nh));
         switch (nh) {
         case 1: launch(down_bs1h_kernel<1>, g, 64 * S, lds, st, a); return hipGetLastError();
         case 2: launch(down_bs1h_kernel<2>, g, 64 * S, lds, st, a); return hipGetLastError();
         case 3: launch(down_bs1h_kernel<3>, g, 64 * S, lds, st, a); return hipGetLastError();
-        case 4: launch(down_bs1h_kernel<4>, g, 64 * S, lds, st, a); return hipGetLastError();
         default: break;
         }
     }

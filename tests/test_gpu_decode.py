@@ -219,11 +219,12 @@ def test_glm_decode_full_size_sampled():
 
 
 
-@pytest.mark.parametrize("H,g", [(1536, 32), (2048, 64), (4096, 32), (6144, 64)])
+@pytest.mark.parametrize("H,g", [(1536, 32), (2048, 64), (4096, 32), (6144, 64), (8192, 32)])
 def test_one_token_half_tile_kernels(H, g):
     # One token, F 2048, 8 routed + 1 shared expert: the down projection runs
-    # over half tiles (H/2048 of them per block, one when H is not a multiple
-    # of 2048) and, for H a multiple of 1024, the shared expert's gate/up over
+    # over half tiles (H/2048 of them per block up to 3, two for H = 8192, one
+    # when H is not a multiple of 2048) and, for H a multiple of 1024, the
+    # shared expert's gate/up over
     # half tile pairs inside the top-k launch.  Full outputs, the SwiGLU rows
     # and their codes of every slot are compared with the oracle.
     F, E, k = 2048, 16, 8
