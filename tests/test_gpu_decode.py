@@ -132,6 +132,27 @@ def test_layer_shared_expert(T, g):
     lay.close()
 
 
+@pytest.mark.parametrize("T,H,E", [(9, 2048, 300), (3, 8192, 40), (20, 1024, 600)])
+def test_layer_token_codes_from_topk_launch(T, H, E):
+    # Two tokens and more: the top-k launch (4, 8 or 16 waves for up to 256,
+    # 512 or 1024 experts) also quantises the tokens.  Its codes and scales
+    # equal the oracle's bit for bit, and the layer output matches.
+    c = Case(60 + T, T, H, 256, E, 4, 1, r=2.5, n_distinct=4)
+    lay = c.layer(max_tokens=32)
+    idx, w, out = lay.forward(lay.x_tensor(c.x))
+    _sync()
+    q_o, s_o = oracle.quant_rows(synth.bf16_bits_to_f32(c.x))
+    q = lay.debug_read(0, (T, H), torch.int8).cpu().numpy()
+    s = lay.debug_read(1, (T,), torch.float32).cpu().numpy()
+    assert np.array_equal(q, np.asarray(q_o, np.int8))
+    assert np.array_equal(s.view(np.uint32), np.asarray(s_o, np.float32).view(np.uint32))
+    idx_o, w_o, out_o = c.oracle_layer()
+    _, _, _, _, ch_o = c.oracle_router()
+    check_routing(idx.cpu().numpy(), w.cpu().numpy(), idx_o, w_o, ch_o)
+    check_out(out.cpu().numpy(), out_o)
+    lay.close()
+
+
 def test_layer_bf16_output():
     c = Case(4, 6, 512, 256, 8, 2, 1, r=1.0)
     lay = c.layer(out_dtype=abi.DT_BF16)
