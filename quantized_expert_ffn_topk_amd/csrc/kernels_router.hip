@@ -73,8 +73,10 @@ hipError_t launch_quant_tokens(const uint16_t *x, int T, int H, int8_t *q, float
 // ---------------------------------------------------------------------------
 // Router logits l[t,e] = sum_k x[t,k]*Wr[e,k] in fp64 (bf16 x fp32 products
 // are exact in fp64).
-// 2-16 tokens: one wave per expert streams its router row with 16-byte loads
-// for up to TB tokens.  Many tokens: the fp64 MFMA below.
+// 2-16 tokens: one block per expert and TB tokens; its four waves split the
+// router row into four K slices, each slice's loads in flight together (one
+// batch of U 256-input steps for H = 6144), and the slices' sums are added in
+// slice order.  Many tokens: the fp64 MFMA below.
 // ---------------------------------------------------------------------------
 template <int TB>
 __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t *__restrict__ x, int T,
@@ -82,10 +84,9 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t *__rest
                                                           int E, double *__restrict__ logits)
 {
     constexpr int U = 6;                         // 256-input steps whose loads fly together
+    __shared__ double part[4][TB];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + wave;
-    if (e >= E)
-        return;
+    const int e = blockIdx.x;
     const int t0 = blockIdx.y * TB;
     const float *w = Wr + (size_t)e * H;
     const uint16_t *xr[TB];
@@ -97,12 +98,13 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t *__rest
     for (int m = 0; m < TB; ++m)
         acc[m] = 0.0;
     const int nk = H / 256;                      // H is a multiple of 256
-    for (int k0 = 0; k0 < nk; k0 += U) {
+    const int k_lo = wave * nk / 4, k_hi = (wave + 1) * nk / 4;   // this wave's steps
+    for (int k0 = k_lo; k0 < k_hi; k0 += U) {
         float4 wv[U];
         uint2 xv[U][TB];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int k = 256 * min(k0 + u, nk - 1) + lane * 4;
+            const int k = 256 * min(k0 + u, k_hi - 1) + lane * 4;   // clamped: in the slice
             wv[u] = *reinterpret_cast<const float4 *>(w + k);
 #pragma unroll
             for (int m = 0; m < TB; ++m)
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t *__rest
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (k0 + u < nk) {
+            if (k0 + u < k_hi) {
 #pragma unroll
                 for (int m = 0; m < TB; ++m) {
                     acc[m] = fma((double)bf16_to_f32(xv[u][m].x & 0xffffu), (double)wv[u].x, acc[m]);
@@ -123,9 +125,14 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const uint16_t *__rest
     }
 #pragma unroll
     for (int m = 0; m < TB; ++m) {
-        double v = wave_sum_d(acc[m]);
-        if (lane == 0 && t0 + m < T)
-            logits[(size_t)(t0 + m) * E + e] = v;
+        const double v = wave_sum_d(acc[m]);
+        if (lane == 0)
+            part[wave][m] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < TB && t0 + (int)threadIdx.x < T) {
+        const int m = threadIdx.x;
+        logits[(size_t)(t0 + m) * E + e] = ((part[0][m] + part[1][m]) + part[2][m]) + part[3][m];
     }
 }
 
@@ -231,7 +238,7 @@ hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *Wr
     if (T <= 0)
         return hipSuccess;
     if (T <= 16) {
-        dim3 grid((E + 3) / 4, (T + 3) / 4);
+        dim3 grid(E, (T + 3) / 4);
         launch(router_gemv_kernel<4>, grid, 256, 0, st, x, T, H, Wr, E, logits);
         return hipGetLastError();
     }
