@@ -21,8 +21,9 @@
 // per chunk and are applied in the conversion, so mixing chunks is exact.
 //
 // Work list: tiles of 16 rows of one expert (mx_tiles); a block covers one row
-// tile and 32 weight tiles (4 waves x 8 tiles of 16 rows).
-//   gate/up: waves hold the gate and up tiles of 4 row pairs; the epilogue is
+// tile and 4 TPW weight tiles (4 waves x TPW tiles of 16 rows; TPW = 8 for
+// gate/up, 4 for down).
+//   gate/up: waves hold the gate and up tiles of TPW/2 row pairs; the epilogue is
 //            h = bf16(fp32(G/(1+exp(-G)) * U)) with G, U the fp32 projections.
 //   down   : Y[slot, n] in fp32, combined afterwards by combine_kernel.
 #include "device_common.h"
@@ -35,7 +36,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int MX_MT = 16;          // activation rows per tile
-constexpr int MX_TPW = 8;          // weight tiles per wave
 
 struct MxArgs {
     Experts ex;
@@ -92,7 +92,7 @@ __device__ __forceinline__ void mx_block_coords(int mt_max, int *nb, int *mt)
     *mt = logical - *nb * mt_max;
 }
 
-template <bool GATEUP>
+template <bool GATEUP, int TPW>
 __global__ __launch_bounds__(256) void mx_proj_kernel(MxArgs a, const int2 *__restrict__ tiles,
                                                       const int32_t *__restrict__ n_tiles,
                                                       int mt_max, int n_groups)
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void mx_proj_kernel(MxArgs a, const int2 *__re
     const int e = tl.x, m0 = tl.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
-    const int t0 = (nb * 4 + wave) * MX_TPW;         // first weight tile of this wave
+    const int t0 = (nb * 4 + wave) * TPW;         // first weight tile of this wave
     if (t0 >= a.n_wtiles)
         return;
     const int cnt = a.rt.cnt[e];
@@ -123,26 +123,26 @@ __global__ __launch_bounds__(256) void mx_proj_kernel(MxArgs a, const int2 *__re
         const int row = a.in_by_token ? slot_r / a.rt.S : slot_r;
         arow = reinterpret_cast<const uint4 *>(a.act + (size_t)row * a.K);
     }
-    const uint4 *wt[MX_TPW];
-    const uint8_t *st[MX_TPW];
+    const uint4 *wt[TPW];
+    const uint8_t *st[TPW];
 #pragma unroll
-    for (int t = 0; t < MX_TPW; ++t) {
+    for (int t = 0; t < TPW; ++t) {
         const int tt = min(t0 + t, a.n_wtiles - 1);  // clamped: loads stay in bounds
         wt[t] = reinterpret_cast<const uint4 *>(blob + a.w_off + (size_t)tt * a.tile_w) + lane;
         st[t] = blob + a.s_off + (size_t)tt * a.tile_s + (size_t)g * 16 + r;
     }
 
-    f32x4 acc[MX_TPW];
+    f32x4 acc[TPW];
 #pragma unroll
-    for (int t = 0; t < MX_TPW; ++t)
+    for (int t = 0; t < TPW; ++t)
         acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int KC = a.K >> 5;
     for (int c0 = 0; c0 < KC; c0 += 4) {
-        uint4 w[MX_TPW];
-        uint32_t s8[MX_TPW];
+        uint4 w[TPW];
+        uint32_t s8[TPW];
 #pragma unroll
-        for (int t = 0; t < MX_TPW; ++t) {
+        for (int t = 0; t < TPW; ++t) {
             w[t] = load_stream16(wt[t] + (size_t)c0 * 16);   // 1 KiB per wave: chunks c0..c0+3, 16 rows
             s8[t] = st[t][(size_t)c0 * 16];
         }
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void mx_proj_kernel(MxArgs a, const int2 *__re
                 av[j] = ap[j];
         }
 #pragma unroll
-        for (int t = 0; t < MX_TPW; ++t) {
+        for (int t = 0; t < TPW; ++t) {
             const float sc = e8m0_scale(s8[t]);
             const uint32_t wd[4] = {w[t].x, w[t].y, w[t].z, w[t].w};
 #pragma unroll
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(256) void mx_proj_kernel(MxArgs a, const int2 *__re
         if (GATEUP) {
             uint16_t *hb = reinterpret_cast<uint16_t *>(a.out) + (size_t)slot * a.ldo;
 #pragma unroll
-            for (int p = 0; p < MX_TPW / 2; ++p) {
+            for (int p = 0; p < TPW / 2; ++p) {
                 const int b = (t0 >> 1) + p;          // gate tile 2b, up tile 2b+1
                 if (2 * b + 1 >= a.n_wtiles)
                     break;
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) void mx_proj_kernel(MxArgs a, const int2 *__re
         } else {
             float *y = reinterpret_cast<float *>(a.out) + (size_t)slot * a.ldo;
 #pragma unroll
-            for (int t = 0; t < MX_TPW; ++t)
+            for (int t = 0; t < TPW; ++t)
                 if (t0 + t < a.n_wtiles)
                     y[16 * (t0 + t) + r] = acc[t][i];
         }
@@ -250,9 +250,11 @@ moe_status mx_ffn_enqueue(moe_ctx *c, const void *x, int T, const moe_layer_weig
     a.out = c->hb;
     a.ldo = F;
     {
-        const int ng = (a.n_wtiles + 4 * MX_TPW - 1) / (4 * MX_TPW);
+        // 8 weight tiles per wave for gate/up (4 ran the same), 4 for down
+        // (8 ran ~2 % slower: the down blocks are shorter, K = F)
+        const int ng = (a.n_wtiles + 4 * 8 - 1) / (4 * 8);
         MX_LAUNCH(MOE_PROF_GATEUP, "gate/up launch",
-                  (launch(mx_proj_kernel<true>, grid8(mt_max * ng), 256, 0, st, a, tl, c->n_tiles,
+                  (launch(mx_proj_kernel<true, 8>, grid8(mt_max * ng), 256, 0, st, a, tl, c->n_tiles,
                           mt_max, ng),
                    hipGetLastError()));
     }
@@ -268,9 +270,9 @@ moe_status mx_ffn_enqueue(moe_ctx *c, const void *x, int T, const moe_layer_weig
     a.out = c->Y;
     a.ldo = H;
     {
-        const int ng = (a.n_wtiles + 4 * MX_TPW - 1) / (4 * MX_TPW);
+        const int ng = (a.n_wtiles + 4 * 4 - 1) / (4 * 4);
         MX_LAUNCH(MOE_PROF_DOWN, "down launch",
-                  (launch(mx_proj_kernel<false>, grid8(mt_max * ng), 256, 0, st, a, tl, c->n_tiles,
+                  (launch(mx_proj_kernel<false, 4>, grid8(mt_max * ng), 256, 0, st, a, tl, c->n_tiles,
                           mt_max, ng),
                    hipGetLastError()));
     }
