@@ -360,7 +360,7 @@ def test_graph_replay_matches_eager():
 
 
 @pytest.mark.parametrize("T,E", [(17, 40), (100, 64), (300, 256), (1100, 48), (5, 300), (40, 513),
-                                 (20, 1024)])
+                                 (20, 1024), (2, 1024), (16, 7)])
 def test_router_logits_many_tokens(T, E):
     # the router GEMV (up to 16 tokens) and the fp64 MFMA router (more), E not
     # a multiple of 16 included, and the block top-k with 4, 8 and 16 waves
