@@ -161,7 +161,7 @@ extern "C" moe_status moe_ctx_create(int32_t device, const moe_layer_desc *desc,
     } while (0)
     ALLOC(c->xq, T * H);
     ALLOC(c->sa, T);
-    ALLOC(c->logits, T * E);
+    ALLOC(c->logits, 2 * T * E);          // two K parts for few tokens
     ALLOC(c->idx, T * k);
     ALLOC(c->gw, T * k);
     ALLOC(c->cnt, E + 1);
@@ -470,7 +470,8 @@ static moe_status router_enqueue(moe_ctx *c, const void *x, int32_t T, const moe
     LAUNCH(MOE_PROF_TOPK, "top-k launch",
            launch_topk(c->logits, w->router_bias, T, d.n_experts, d.top_k, d.routed_scale, idx,
                        gw, st, q ? static_cast<const uint16_t *>(x) : nullptr, d.hidden,
-                       q ? c->xq : nullptr, q ? c->sa : nullptr));
+                       q ? c->xq : nullptr, q ? c->sa : nullptr,
+                       router_ksplit(T, d.hidden, d.n_experts)));
     return MOE_OK;
 }
 

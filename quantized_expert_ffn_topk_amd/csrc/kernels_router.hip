@@ -156,7 +156,9 @@ __global__ __launch_bounds__(64 * KS) void router_mfma_kernel(const uint16_t *__
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
     const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16 * MT;
-    const int KL = H / KS, kb = wave * KL;
+    // gridDim.z K parts on separate blocks, part z written to logits + z*T*E
+    const int KL = H / (KS * gridDim.z), kb = blockIdx.z * (H / gridDim.z) + wave * KL;
+    logits += (size_t)blockIdx.z * T * E;
     const float *wrow = Wr + (size_t)min(e0 + r, E - 1) * H + kb + 8 * g;   // clamped rows
     const uint16_t *xrow[MT];
 #pragma unroll
@@ -232,6 +234,21 @@ __global__ __launch_bounds__(64 * KS) void router_mfma_kernel(const uint16_t *__
         }
 }
 
+// Few 16-token tiles (fewer than 128 blocks): the two K halves go to separate
+// blocks, so twice as many CUs run the fp64 MFMA; the top-k launch adds the
+// two partial logits in order.  Needs whole 32-input steps per wave.
+int router_ksplit(int T, int H, int E)
+{
+    if (T <= 16 || T >= 1024)
+        return 1;
+    const int ne = (E + 15) / 16, H32 = H / 32;
+    const long tiles = (long)ne * ((T + 15) / 16);
+    if (tiles >= 128)
+        return 1;
+    const int ks = (H32 % 16) ? 8 : 16;
+    return (H32 % (2 * ks) == 0) ? 2 : 1;
+}
+
 hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *Wr, int E,
                                 double *logits, hipStream_t st)
 {
@@ -252,7 +269,7 @@ hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *Wr
         dim3 grid(ne, (T + 63) / 64);
         launch(router_mfma_kernel<4, 4>, grid, 256, 0, st, x, T, H, Wr, E, logits);
     } else {
-        dim3 grid(ne, (T + 15) / 16);
+        dim3 grid(ne, (T + 15) / 16, router_ksplit(T, H, E));
         const long tiles = (long)grid.x * grid.y;
         if (tiles >= 512 || H32 % 16)
             launch(router_mfma_kernel<1, 8>, grid, 512, 0, st, x, T, H, Wr, E, logits);
@@ -267,13 +284,13 @@ hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *Wr
 // With xq set the block also quantises token t (the rule of
 // quant_tokens_kernel), its row loads issued before the selection.
 template <int NW>
-__global__ __launch_bounds__(64 * NW) void topk_block_kernel(const double *__restrict__ logits,
+__global__ __launch_bounds__(64 * NW) void topk_block_kernel(double *__restrict__ logits,
                                                              const float *__restrict__ bias, int E,
                                                              int k, float r, int32_t *__restrict__ idx,
                                                              float *__restrict__ w,
                                                              const uint16_t *__restrict__ x, int H,
                                                              int8_t *__restrict__ xq,
-                                                             float *__restrict__ sa)
+                                                             float *__restrict__ sa, int kparts)
 {
     constexpr int NT = 64 * NW;
     constexpr int XL = 8192 / (8 * NT);          // 16-byte pieces per thread, H <= 8192
@@ -291,7 +308,11 @@ __global__ __launch_bounds__(64 * NW) void topk_block_kernel(const double *__res
     double c = -INFINITY;
     int ci = INT_MAX;
     if (tid < E) {
-        const double l = logits[(size_t)t * E + tid];
+        double l = logits[(size_t)t * E + tid];
+        if (kparts == 2) {                       // two K halves: summed in order, kept
+            l = l + logits[(size_t)gridDim.x * E + (size_t)t * E + tid];
+            logits[(size_t)t * E + tid] = l;
+        }
         const double sv = 1.0 / (1.0 + exp(-l));
         const double cv = sv + (double)bias[tid];
         s_s[tid] = sv;
@@ -344,19 +365,22 @@ __global__ __launch_bounds__(64 * NW) void topk_block_kernel(const double *__res
         sa[t] = sc;
 }
 
-hipError_t launch_topk(const double *logits, const float *bias, int T, int E, int k, float r,
+hipError_t launch_topk(double *logits, const float *bias, int T, int E, int k, float r,
                        int32_t *idx, float *w, hipStream_t st, const uint16_t *x, int H,
-                       int8_t *xq, float *sa)
+                       int8_t *xq, float *sa, int kparts)
 {
     if (T <= 0)
         return hipSuccess;
     // E <= 1024 and k <= 16 (checked at context creation)
     if (E <= 256)
-        launch(topk_block_kernel<4>, T, 256, 0, st, logits, bias, E, k, r, idx, w, x, H, xq, sa);
+        launch(topk_block_kernel<4>, T, 256, 0, st, logits, bias, E, k, r, idx, w, x, H, xq, sa,
+               kparts);
     else if (E <= 512)
-        launch(topk_block_kernel<8>, T, 512, 0, st, logits, bias, E, k, r, idx, w, x, H, xq, sa);
+        launch(topk_block_kernel<8>, T, 512, 0, st, logits, bias, E, k, r, idx, w, x, H, xq, sa,
+               kparts);
     else
-        launch(topk_block_kernel<16>, T, 1024, 0, st, logits, bias, E, k, r, idx, w, x, H, xq, sa);
+        launch(topk_block_kernel<16>, T, 1024, 0, st, logits, bias, E, k, r, idx, w, x, H, xq, sa,
+               kparts);
     return hipGetLastError();
 }
 

@@ -186,13 +186,16 @@ inline void launch(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t st, 
 // ---------------------------------------------------------------------------
 hipError_t launch_quant_tokens(const uint16_t *x, int T, int H, int8_t *q, float *s,
                                hipStream_t st);
+// K parts of the router logits for T tokens (1 or 2; with 2 the logits
+// buffer holds 2*T*E partials until the top-k launch sums them).
+int router_ksplit(int T, int H, int E);
 hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *Wr, int E,
                                 double *logits, hipStream_t st);
 // With xq/sa set, the launch also quantises the T token rows of x (H <= 8192)
 // into xq/sa as launch_quant_tokens does.
-hipError_t launch_topk(const double *logits, const float *bias, int T, int E, int k, float r,
+hipError_t launch_topk(double *logits, const float *bias, int T, int E, int k, float r,
                        int32_t *idx, float *w, hipStream_t st, const uint16_t *x = nullptr,
-                       int H = 0, int8_t *xq = nullptr, float *sa = nullptr);
+                       int H = 0, int8_t *xq = nullptr, float *sa = nullptr, int kparts = 1);
 hipError_t launch_permute(const int32_t *idx, int T, int k, int E, int n_shared,
                           int32_t *cnt, int32_t *list, int list_stride, int32_t *active,
                           int32_t *n_active, uint32_t *done_counter, hipStream_t st);
