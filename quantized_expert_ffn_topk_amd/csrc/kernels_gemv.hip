@@ -447,7 +447,46 @@ __global__ __launch_bounds__(256) void requant_kernel(const float *__restrict__ 
 {
     __shared__ float red[4];
     const int row = blockIdx.x;
-    requant_row<false>(h + (size_t)row * F, F, q + (size_t)row * F, s + row, red);
+    const float *hr = h + (size_t)row * F;
+    if (F > 4096) {
+        requant_row<false>(hr, F, q + (size_t)row * F, s + row, red);
+        return;
+    }
+    // up to 4096 values: every load of the thread in flight at once, the
+    // row read once
+    float4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int i = threadIdx.x * 4 + 1024 * j;
+        v[j] = (i < F) ? *reinterpret_cast<const float4 *>(hr + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+    amax = block_max_256(amax, red);
+    float inv = 0.0f, sc = 0.0f;
+    if (amax > 0.0f) {
+        inv = 127.0f / amax;
+        sc = amax / 127.0f;
+    }
+    int8_t *qr = q + (size_t)row * F;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int i = threadIdx.x * 4 + 1024 * j;
+        if (i < F) {
+            const float vv[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+            uint32_t packed = 0u;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const float rr = fminf(fmaxf(rintf(vv[b] * inv), -127.0f), 127.0f);
+                packed |= ((uint32_t)(int)rr & 0xffu) << (8 * b);
+            }
+            *reinterpret_cast<uint32_t *>(qr + i) = packed;
+        }
+    }
+    if (threadIdx.x == 0)
+        s[row] = sc;
 }
 
 hipError_t launch_requant(const float *h, int rows, int F, int8_t *q, float *s, hipStream_t st)
