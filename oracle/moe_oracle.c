@@ -119,6 +119,12 @@ static double sigmoid64(double l)
     return 1.0 / (1.0 + exp(-l));
 }
 
+/* the value a biased score is ranked by: itself, or -inf for NaN */
+static double rank_key(double c)
+{
+    return isnan(c) ? -INFINITY : c;
+}
+
 void orc_router(int T, int H, int E, int k, float r,
                 const uint16_t *x, const float *Wr, const float *b,
                 int32_t *idx, float *w,
@@ -144,13 +150,15 @@ void orc_router(int T, int H, int E, int k, float r,
             if (choice) choice[(size_t)t * E + e] = c[e];
         }
         /* k rounds of "largest c among the experts not yet taken"; scanning
-         * e upwards with a strict > keeps the lowest index on ties. */
+         * e upwards with a strict > keeps the lowest index on ties.  A NaN c
+         * ranks as -inf (reading: an undefined score never wins a place over
+         * a defined one). */
         for (int i = 0; i < k; ++i) {
             int best = -1;
             for (int e = 0; e < E; ++e) {
                 if (taken[e])
                     continue;
-                if (best < 0 || c[e] > c[best])
+                if (best < 0 || rank_key(c[e]) > rank_key(c[best]))
                     best = e;
             }
             taken[best] = 1;

@@ -53,7 +53,7 @@ void orc_quant_row(const float *v, int K, int8_t *q, float *s);
 /* For T tokens x[T,H] (bf16 bits), router weights Wr[E,H] (fp32) and selection
  * bias b[E] (fp32):  l = x . Wr_e (fp64), s = 1/(1+exp(-l)), c = s + b.
  * idx[T,k] = the k experts with the largest c, ties to the lower index, in rank
- * order; w[T,k] = s_idx / sum(s_idx) * r.  logits/scores/choice may be NULL
+ * order (a NaN c ranks as -inf); w[T,k] = s_idx / sum(s_idx) * r.  logits/scores/choice may be NULL
  * ([T,E] fp64 each). */
 void orc_router(int T, int H, int E, int k, float r,
                 const uint16_t *x, const float *Wr, const float *b,

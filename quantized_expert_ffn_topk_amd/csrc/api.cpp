@@ -669,6 +669,17 @@ extern "C" moe_status moe_layer_forward(moe_ctx *ctx, const void *x, int32_t T,
         return MOE_OK;
     if (!out)
         return fail(MOE_E_INVAL, "out is NULL");
+    if (cache) {
+        s = cache_check_for_layer(cache, ctx->d, layer, T);
+        if (s)
+            return s;
+    }
+    if (!w->router_w || !w->router_bias)
+        return fail(MOE_E_INVAL, "router weights are NULL");
+    if (ctx->d.n_shared && !w->shared)
+        return fail(MOE_E_INVAL, "shared expert blob is NULL");
+    if (!cache && !w->expert_ptrs)
+        return fail(MOE_E_INVAL, "expert_ptrs is NULL");
     hipStream_t st = static_cast<hipStream_t>(stream);
     int32_t *idx = idx_out ? idx_out : ctx->idx;
     float *gw = gate_w_out ? gate_w_out : ctx->gw;

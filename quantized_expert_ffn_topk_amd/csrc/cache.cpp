@@ -456,12 +456,14 @@ namespace moe {
 // the host (this is the call's one host synchronisation), the distinct experts
 // are staged in order of first appearance, and the layer's device table is
 // returned.
-moe_status cache_demand_for_layer(moe_cache *c, const moe_layer_desc &d, int layer,
-                                  const int32_t *idx_dev, int T, hipStream_t compute,
-                                  const void *const **table)
+moe_status cache_check_for_layer(const moe_cache *c, const moe_layer_desc &d, int layer, int T)
 {
+    if (!c)
+        return fail(MOE_E_INVAL, "cache is NULL");
     if (c->d.backend != MOE_CACHE_BACKEND_HIP)
         return fail(MOE_E_INVAL, "moe_layer_forward needs a cache with the HIP backend");
+    if (layer < 0 || layer >= c->d.n_layers)
+        return fail(MOE_E_INVAL, "layer %d out of range [0,%d)", layer, c->d.n_layers);
     if (c->d.n_experts != d.n_experts)
         return fail(MOE_E_INVAL, "cache has %d experts per layer, layer has %d",
                     c->d.n_experts, d.n_experts);
@@ -469,9 +471,20 @@ moe_status cache_demand_for_layer(moe_cache *c, const moe_layer_desc &d, int lay
     if (c->d.blob_bytes != blob)
         return fail(MOE_E_INVAL, "cache blob size %zu != layer blob size %zu", c->d.blob_bytes,
                     blob);
+    if ((int64_t)T * d.top_k > c->ids_cap)
+        return fail(MOE_E_INVAL, "T*k=%lld exceeds the cache's id buffer (%d)",
+                    (long long)T * d.top_k, c->ids_cap);
+    return MOE_OK;
+}
+
+moe_status cache_demand_for_layer(moe_cache *c, const moe_layer_desc &d, int layer,
+                                  const int32_t *idx_dev, int T, hipStream_t compute,
+                                  const void *const **table)
+{
+    moe_status st = cache_check_for_layer(c, d, layer, T);
+    if (st)
+        return st;
     const int n = T * d.top_k;
-    if (n > c->ids_cap)
-        return fail(MOE_E_INVAL, "T*k=%d exceeds the cache's id buffer (%d)", n, c->ids_cap);
     hipError_t e = hipMemcpyAsync(c->ids_pinned, idx_dev, (size_t)n * 4, hipMemcpyDeviceToHost,
                                   compute);
     if (e == hipSuccess)
@@ -489,7 +502,7 @@ moe_status cache_demand_for_layer(moe_cache *c, const moe_layer_desc &d, int lay
             uniq.push_back(v);
         }
     }
-    moe_status st = stage_demand(c, layer, uniq.data(), (int)uniq.size(), compute, nullptr);
+    st = stage_demand(c, layer, uniq.data(), (int)uniq.size(), compute, nullptr);
     if (st)
         return st;
     *table = moe_cache_table(c, layer);

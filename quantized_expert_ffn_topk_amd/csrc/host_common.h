@@ -92,7 +92,11 @@ moe_status mx_ffn_enqueue(moe_ctx *c, const void *x, int T, const moe_layer_weig
 // small helpers (kernels_router.hip)
 hipError_t launch_set_i32(int32_t *p, int32_t v, hipStream_t st);
 
-// cache (cache.cpp): DEMAND stage of the routed experts of `layer` for the
+// cache (cache.cpp): the checks of a moe_layer_forward call with a cache
+// (backend, layer in range, shapes, id buffer), run before anything is enqueued
+moe_status cache_check_for_layer(const moe_cache *cache, const moe_layer_desc &d, int layer,
+                                 int T);
+// DEMAND stage of the routed experts of `layer` for the
 // T*k device ids in idx; returns the device pointer table for the layer.
 moe_status cache_demand_for_layer(moe_cache *cache, const moe_layer_desc &d, int layer,
                                   const int32_t *idx_dev, int T, hipStream_t compute,

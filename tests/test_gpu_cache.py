@@ -139,3 +139,23 @@ def test_failed_copy_leaves_slot_empty_and_retry_works():
         abi.moe_cache_release(stk.cache, 1)
     finally:
         stk.close()
+
+
+@pytest.mark.parametrize("layer", [-1, L_])
+def test_layer_forward_rejects_layer_out_of_range_before_enqueue(layer):
+    # a layer index outside [0, n_layers) is an argument error caught before
+    # the router is enqueued: the caller's idx / gate_w / out stay untouched
+    stk = Stack(8)
+    try:
+        idx = torch.full((1, K), -7, dtype=torch.int32, device="cuda")
+        gw = torch.full((1, K), -7.0, dtype=torch.float32, device="cuda")
+        out = torch.full((1, H), -7.0, dtype=torch.float32, device="cuda")
+        x = stk.ref[0].x_tensor(synth.activations(9, 1, H))
+        with pytest.raises(abi.MoEError) as ei:
+            abi.moe_layer_forward(stk.ctx, x, 1, stk.wts[0], stk.cache, layer, idx, gw, out)
+        assert ei.value.status == abi.E_INVAL
+        torch.cuda.synchronize()
+        assert bool((idx == -7).all()) and bool((gw == -7.0).all()) and bool((out == -7.0).all())
+        assert abi.moe_cache_stats_get(stk.cache)["bytes_copied"] == 0
+    finally:
+        stk.close()

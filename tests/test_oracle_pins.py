@@ -212,6 +212,30 @@ def test_router_weights_ignore_bias(orc):
         assert np.all(np.diff(s) <= 0)            # rank order is by c = s + 4
 
 
+def test_router_nan_choice_ranks_as_minus_infinity(orc):
+    # A NaN bias makes c NaN; by the reading on undefined scores it ranks as
+    # -inf: never above a defined c, and among -inf values the lower index
+    # first.  The expected order is a plain sort over (-key, index).
+    r = np.random.default_rng(29)
+    T, E, H = 3, 10, 64
+    x = synth.f32_to_bf16_bits(r.standard_normal((T, H)).astype(np.float32))
+    Wr = (r.standard_normal((E, H)) * 0.1).astype(np.float32)
+    b = (r.standard_normal(E) * 0.01).astype(np.float32)
+    b[2] = 5.0            # would win every token
+    b[0] = np.nan
+    b[2] = np.nan
+    b[7] = -np.inf
+    for k in (3, E):
+        idx, w, lg, sc, ch = orc.router(x, Wr, b, k, 1.0, want=True)
+        for t in range(T):
+            key = [(-np.inf if np.isnan(ch[t, e]) else ch[t, e]) for e in range(E)]
+            want = sorted(range(E), key=lambda e: (-key[e], e))[:k]
+            assert idx[t].tolist() == want
+        if k == E:
+            # the three undefined or -inf experts come last, lowest index first
+            assert idx[:, -3:].tolist() == [[0, 2, 7]] * T
+
+
 # ---------------------------------------------------------------------------
 # int4 x int8 projection
 # ---------------------------------------------------------------------------
@@ -540,3 +564,44 @@ def test_mx_layer_runs_and_routes(orc):
         for i in range(k):
             acc = acc + float(w[t, i]) * orc.mx_expert(xf[t], exps[idx[t, i]])["y"].astype(np.float64)
         assert np.array_equal(out[t], acc.astype(np.float32))
+
+
+def _mx_deq(orc, c, e):
+    # OCP MX dequantisation written out in numpy: E2M1 value times 2^(E8M0-127)
+    v = np.array([orc.e2m1_value(i) for i in range(16)], np.float64)[c]
+    return v * np.repeat(np.ldexp(1.0, e.astype(np.int64) - 127), 32, axis=1)
+
+
+def _mx_expert_fp64(orc, a, ex):
+    # fp64 dequantised SwiGLU expert with h rounded to bf16 (the MXFP4 reading)
+    G = _mx_deq(orc, ex["c_gate"], ex["e_gate"]) @ a.astype(np.float64)
+    U = _mx_deq(orc, ex["c_up"], ex["e_up"]) @ a.astype(np.float64)
+    h = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits((G / (1 + np.exp(-G)) * U).astype(np.float32)))
+    return _mx_deq(orc, ex["c_down"], ex["e_down"]) @ h.astype(np.float64)
+
+
+def test_mx_layer_identical_experts(orc):
+    # Every routed expert identical: out = Y_sh + (sum w) * Y = Y_sh + r * Y,
+    # with Y and Y_sh from the numpy dequantised reference above (not from the
+    # oracle's own expert), so a dropped shared term, a wrong scale r or a
+    # combine that misses a rank fails.
+    H, F, T, E, k, rs = 256, 64, 3, 7, 3, 1.75
+    x = synth.activations(19, T, H)
+    Wr, _ = synth.router_weights(19, E, H)
+    b = synth.uniform_bias(19, E)
+    one = synth.expert_mxfp4(19, 0, H, F)
+    shared = synth.expert_mxfp4(19, -1, H, F)
+    _, w, out = orc.mx_layer(x, Wr, b, [one] * E, shared, k, rs)
+    xf = synth.bf16_bits_to_f32(x)
+    for t in range(T):
+        y = _mx_expert_fp64(orc, xf[t], one)
+        ysh = _mx_expert_fp64(orc, xf[t], shared)
+        want = ysh + rs * y
+        assert abs(float(w[t].astype(np.float64).sum()) - rs) <= 1e-6 * rs
+        # (measured agreement ~3e-8 of the largest output on these inputs)
+        assert np.allclose(out[t], want, rtol=1e-5, atol=1e-5 * np.abs(want).max())
+    # and without the shared expert the output is r * Y alone
+    _, _, out0 = orc.mx_layer(x, Wr, b, [one] * E, None, k, rs)
+    for t in range(T):
+        want = rs * _mx_expert_fp64(orc, xf[t], one)
+        assert np.allclose(out0[t], want, rtol=1e-5, atol=1e-5 * np.abs(want).max())
