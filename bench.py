@@ -12,10 +12,11 @@ routed gate/up + SwiGLU, then requantisation, down projections and combine.
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 
 Prints one JSON line.  `value` is layer tokens/s with all inputs resident in
-HBM; `roofline` covers the dominant kernel (the routed gate/up projection), its
-duration the average of the kernel's own dispatch timestamps (HIP events)
-over a pass of the same K steps run back to back; `cpu_baseline` is the plain C oracle on a
-bounded sample of the same workload, on this host.
+HBM; `roofline` covers the decode GEMV projections (the routed gate/up launch
+and the down launch, which move 90 % of a step's bytes), their durations the
+average of each kernel's own dispatch timestamps (HIP events) over a pass of
+the same K steps run back to back; `cpu_baseline` is the plain C oracle on a
+bounded sample of the same workload, on this host, pinned to one core.
 """
 import argparse
 import json
@@ -53,8 +54,9 @@ TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_glm_bs1_hbm_traffic.md")
 
 
 def measured_traffic():
-    """HBM bytes per gate/up launch from the committed rocprofv3 counter
-    summary, or None when a kernel source listed there has changed since."""
+    """HBM bytes per launch of the decode projections ({"gateup": B, "down": B})
+    from the committed rocprofv3 counter summary, or None when a kernel source
+    listed there has changed since the counters were taken."""
     import hashlib
     try:
         text = open(TRAFFIC_RECORD).read()
@@ -246,12 +248,56 @@ def run_prefill(args, lay):
     prof = abi.moe_ctx_profile_read(ctx)
     abi.moe_ctx_profile(ctx, False)
     loads = np.bincount(idx.cpu().numpy().ravel(), minlength=E)
-    abi.moe_ctx_destroy(ctx)
     kus = {k: 1e3 * v[0] / v[1] for k, v in prof.items() if v[1]}
     rows = T * (K_TOP + 1)
     ops = 2.0 * rows * (2 * F * H + H * F)                 # int8 MFMA operations (2 per MAC)
     gemm_us = kus.get("gateup", 0.0) + kus.get("down", 0.0)
     sorted_loads = np.sort(loads)[::-1]
+
+    # The grouped GEMMs split by expert size: the same expert FFN call on the
+    # last routing, once with only the entries of experts with >= 256 rows
+    # (the others set to -1, which adds nothing), once with every entry, and
+    # once with none (the shared expert alone, 4096 rows, runs in all three).
+    # Head = big routed experts + the shared expert; tail = the rest, timed as
+    # the difference of the first two.
+    x_last = xs[(n - 1) % 2]
+    ig = idx.clone()
+    head_mask = torch.from_numpy(loads >= 256).to(lay.dev)
+    idx_head = torch.where(head_mask[ig.long()], ig, torch.full_like(ig, -1))
+    idx_none = torch.full_like(ig, -1)
+
+    def ffn_gemm_us(ix):
+        abi.moe_expert_ffn(ctx, x_last, T, wts, ix, w, out, sh)
+        torch.cuda.synchronize()
+        abi.moe_ctx_profile(ctx, True)
+        abi.moe_ctx_profile_read(ctx)
+        for _ in range(n):
+            abi.moe_expert_ffn(ctx, x_last, T, wts, ix, w, out, sh)
+        torch.cuda.synchronize()
+        pr = abi.moe_ctx_profile_read(ctx)
+        abi.moe_ctx_profile(ctx, False)
+        return sum(1e3 * pr[k][0] / pr[k][1] for k in ("gateup", "down") if pr[k][1])
+
+    t_all = ffn_gemm_us(ig)
+    t_head = ffn_gemm_us(idx_head)
+    t_shared = ffn_gemm_us(idx_none)
+    abi.moe_ctx_destroy(ctx)
+    rows_head = int(loads[loads >= 256].sum()) + T
+    rows_tail = int(loads[loads < 256].sum())
+    ops_row = 2.0 * (2 * F * H + H * F)
+    split = {
+        "method": "expert FFN calls on the same routing with only the entries of experts "
+                  "with >= 256 rows kept, with all, and with none (shared expert only); "
+                  "tail time = all - head",
+        "gemm_us_all": t_all,
+        "head": {"experts": int((loads >= 256).sum()) + 1, "rows": rows_head, "gemm_us": t_head,
+                 "frac": ops_row * rows_head / (t_head * 1e-6) / 1e12 / INT8_PEAK_TOPS},
+        "tail": {"experts": int(((loads > 0) & (loads < 256)).sum()), "rows": rows_tail,
+                 "gemm_us": t_all - t_head,
+                 "frac": (ops_row * rows_tail / ((t_all - t_head) * 1e-6) / 1e12 / INT8_PEAK_TOPS
+                          if t_all > t_head else None)},
+        "shared_only_gemm_us": t_shared,
+    }
     return {
         "workload": "same layer, prefill of %d tokens, selection bias skewing loads like "
                     "Zipf(1.1)" % T,
@@ -261,7 +307,8 @@ def run_prefill(args, lay):
         "int8_mfma": {"ops_per_call": ops, "gemm_us": gemm_us,
                       "achieved_TOPS": ops / (gemm_us * 1e-6) / 1e12,
                       "peak_TOPS": INT8_PEAK_TOPS,
-                      "frac": ops / (gemm_us * 1e-6) / 1e12 / INT8_PEAK_TOPS},
+                      "frac": ops / (gemm_us * 1e-6) / 1e12 / INT8_PEAK_TOPS,
+                      "by_expert_size": split},
         "kernels_us": {k: round(v, 2) for k, v in kus.items()},
         "expert_loads": {"max": int(loads.max()), "empty": int((loads == 0).sum()),
                          "top8_share": float(sorted_loads[:8].sum() / loads.sum()),
@@ -344,6 +391,64 @@ def run_mx(args):
     }
 
 
+TINY = dict(T=16, H=2048, F=1024, E=64, k=8, r=1.0)
+
+
+def build_tiny(args):
+    from quantized_expert_ffn_topk_amd import synth
+    from quantized_expert_ffn_topk_amd.layer import Layer, make_desc
+    c = TINY
+    D = args.distinct
+    distinct = [synth.expert_int4(1, e, c["H"], c["F"], G) for e in range(D)]
+    Wr, b = synth.router_weights(1, c["E"], c["H"])
+    emap = [e % D for e in range(c["E"])]
+    desc = make_desc(c["H"], c["F"], c["E"], c["k"], 0, G, c["r"])
+    lay = Layer(desc, Wr, b, distinct, None, emap, max_tokens=c["T"])
+    return lay, dict(distinct=distinct, Wr=Wr, b=b, emap=emap)
+
+
+def run_tiny(args, tl):
+    """The tiny OLMoE-like layer: 16 tokens per call, hidden 2048, 64 routed
+    experts, FFN 1024, top-8, no shared expert.  Its 64 experts (226 MB) fit
+    in the 256 MB Infinity Cache, so the line carries no HBM claim."""
+    import torch
+    from quantized_expert_ffn_topk_amd import abi, synth
+    c = TINY
+    T = c["T"]
+    xs = [tl.x_tensor(synth.activations(40 + i, T, c["H"])) for i in range(4)]
+    idx, w, out = tl._outs(T)
+    stream = torch.cuda.Stream()
+    sh = abi.stream_handle(stream)
+
+    def call(i):
+        abi.moe_layer_forward(tl.ctx, xs[i % 4], T, tl.weights, None, 0, idx, w, out, sh)
+
+    for i in range(10):
+        call(i)
+    torch.cuda.synchronize()
+    n = 200
+    t0 = time.perf_counter()
+    for i in range(n):
+        call(i)
+    stream.synchronize()
+    dt = (time.perf_counter() - t0) / n
+    abi.moe_ctx_profile(tl.ctx, True)
+    abi.moe_ctx_profile_read(tl.ctx)
+    for i in range(n):
+        call(i)
+    torch.cuda.synchronize()
+    prof = abi.moe_ctx_profile_read(tl.ctx)
+    abi.moe_ctx_profile(tl.ctx, False)
+    return {
+        "workload": "tiny OLMoE-like layer: 16 tokens per call, hidden 2048, 64 routed experts, "
+                    "FFN 1024 SwiGLU, int4 group-32, top-8, no shared expert, routed scale 1.0, "
+                    "bias N(0,0.01); expert set Infinity-Cache resident (no HBM claim)",
+        "tokens_per_s": T / dt,
+        "us_per_call": 1e6 * dt,
+        "kernels_us": {k: round(1e3 * v[0] / v[1], 2) for k, v in prof.items() if v[1]},
+    }
+
+
 def run_stream(args, lay, W):
     """Expert streaming: 16 GLM-shaped layers whose 4096 routed experts live in
     pinned host memory behind a 24 GiB HBM cache (global LRU), decode batch 1,
@@ -396,10 +501,38 @@ def run_stream(args, lay, W):
         stream.synchronize()
         dt = time.perf_counter() - t0
         st = abi.moe_cache_stats_get(cache)
-        abi.moe_ctx_destroy(ctx)
         abi.moe_cache_destroy(cache)
+
+        # the same layer calls with every expert resident (the layer's own 256
+        # device blobs, no cache) and the same host synchronisation on the
+        # routing ids per layer: the difference is the time lost to staging
+        def resident_call(t, l):
+            wts = abi.moe_layer_weights(lay.Wr.data_ptr(), bias[t, l].data_ptr(),
+                                        lay.ptrs.data_ptr(), lay.shared_blob.data_ptr())
+            abi.moe_layer_forward(ctx, xs[t * L + l:t * L + l + 1], 1, wts, None, l, idx, w, out, sh)
+            stream.synchronize()
+
+        for t in range(warm):
+            for l in range(L):
+                resident_call(t, l)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(warm, steps):
+            for l in range(L):
+                resident_call(t, l)
+        stream.synchronize()
+        dt_res = time.perf_counter() - t0
+        abi.moe_ctx_destroy(ctx)
     finally:
         abi.moe_host_free_pinned(host)
+    # the lookahead predictor against the next layer's actual experts
+    hit = tot_p = tot_a = 0
+    for t in range(warm, steps):
+        for l in range(L - 1):
+            p_set, a_set = set(predict[t, l].tolist()), set(demand[t, l + 1].tolist())
+            hit += len(p_set & a_set)
+            tot_p += len(p_set)
+            tot_a += len(a_set)
     # pinned host -> device ceiling on this machine, same blob size
     src = torch.empty(blob * 32, dtype=torch.uint8, pin_memory=True)
     dst = torch.empty(blob * 32, dtype=torch.uint8, device=lay.dev)
@@ -420,44 +553,137 @@ def run_stream(args, lay, W):
                                                                                st["n_slots"]),
         "tokens_per_s": n / dt,
         "ms_per_token": 1e3 * dt / n,
+        "resident_ms_per_token": 1e3 * dt_res / n,
+        "stall_us_per_layer": 1e6 * (dt - dt_res) / (n * L),
         "h2d_GBs": st["bytes_copied"] / dt / 1e9,
+        "h2d_GBs_copy_busy": (st["bytes_copied"] / (st["copy_busy_ms"] * 1e-3) / 1e9
+                              if st["copy_busy_ms"] > 0 else None),
+        "copy_busy_share": st["copy_busy_ms"] * 1e-3 / dt,
         "h2d_pinned_ceiling_GBs": ceil_gbs,
         "demand_hit_rate": st["demand_hits"] / dem if dem else None,
         "prefetch_precision": (st["prefetch_used"] / st["prefetch_issued"]
                                if st["prefetch_issued"] else None),
+        # share of the would-be misses that a prefetch turned into hits
+        "prefetch_coverage": (st["prefetch_used"] / (st["prefetch_used"] + st["demand_misses"])
+                              if st["prefetch_used"] + st["demand_misses"] else None),
+        "predictor": {"precision": hit / tot_p if tot_p else None,
+                      "recall": hit / tot_a if tot_a else None},
         "misses_per_token": st["demand_misses"] / n,
         "stats": st,
     }
 
 
+class _one_core:
+    """Pins the calling thread (the one that runs the oracle through ctypes)
+    to a single core for the duration of the block."""
+
+    def __enter__(self):
+        self.old = os.sched_getaffinity(0)
+        self.core = max(self.old)
+        os.sched_setaffinity(0, {self.core})
+        return self
+
+    def __exit__(self, *exc):
+        os.sched_setaffinity(0, self.old)
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(args, lay, W):
-    """The plain C oracle (single thread) on a bounded sample of decode steps."""
+    """The plain C oracle (single thread, pinned to one core) on a bounded
+    sample of decode steps."""
     import oracle
     from quantized_expert_ffn_topk_amd import synth
     oracle.lib()
     xs = synth.activations(2, args.cpu_steps_max, H)
     emap = [e % args.distinct for e in range(E)]
-    t0 = time.perf_counter()
-    n = 0
-    while n < args.cpu_steps_max:
-        oracle.layer(xs[n:n + 1], W["Wr"], W["b"], W["distinct"], W["shared"], K_TOP, R_SCALE, G,
-                     expert_map=emap)
-        n += 1
-        if time.perf_counter() - t0 > args.cpu_seconds and n >= 2:
-            break
-    dt = time.perf_counter() - t0
-    cpu = "unknown"
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                cpu = line.split(":", 1)[1].strip()
+    with _one_core() as pin:
+        t0 = time.perf_counter()
+        n = 0
+        while n < args.cpu_steps_max:
+            oracle.layer(xs[n:n + 1], W["Wr"], W["b"], W["distinct"], W["shared"], K_TOP, R_SCALE,
+                         G, expert_map=emap)
+            n += 1
+            if time.perf_counter() - t0 > args.cpu_seconds and n >= 2:
                 break
-    except OSError:
-        pass
+        dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": "%d decode steps (batch 1) of the same layer, full 6144-wide output, "
-                      "single-threaded C (gcc -O2) on %s; host has %d logical CPUs" % (
-                          n, cpu, os.cpu_count() or 0)}
+                      "single-threaded C (gcc -O2) pinned to core %d of %s; host has %d logical "
+                      "CPUs" % (n, pin.core, _cpu_model(), os.cpu_count() or 0)}
+
+
+def cpu_baselines_other(args, W, TW):
+    """The oracle on each of the other workloads, pinned to one core, on
+    bounded samples: the tiny layer in full (16 tokens), prefill tokens of the
+    GLM-shaped layer under the Zipf bias (8 tokens in full, extrapolated per
+    token, and the router over 512 tokens), one MXFP4 wide-layer token in full,
+    and the cache state machine over the whole streaming trace."""
+    import oracle
+    from quantized_expert_ffn_topk_amd import synth
+    oracle.lib()
+    res = {}
+    with _one_core():
+        c = TINY
+        x = synth.activations(41, c["T"], c["H"])
+        t0 = time.perf_counter()
+        oracle.layer(x, TW["Wr"], TW["b"], TW["distinct"], None, c["k"], c["r"], G,
+                     expert_map=TW["emap"])
+        dt = time.perf_counter() - t0
+        res["tiny"] = {"value": c["T"] / dt, "unit": "tokens/s",
+                       "sample": "the whole 16-token call, full output"}
+
+        bz = synth.zipf_bias(0, E)
+        xp = synth.activations(10, 512, H)
+        emap = [e % args.distinct for e in range(E)]
+        nt = 8
+        t0 = time.perf_counter()
+        oracle.layer(xp[:nt], W["Wr"], bz, W["distinct"], W["shared"], K_TOP, R_SCALE, G,
+                     expert_map=emap)
+        dt = time.perf_counter() - t0
+        t1 = time.perf_counter()
+        oracle.router(xp, W["Wr"], bz, K_TOP, R_SCALE)
+        dr = time.perf_counter() - t1
+        res["prefill"] = {"value": nt / dt, "unit": "tokens/s",
+                          "extrapolated_ms_per_4096": 1e3 * dt / nt * 4096,
+                          "router_tokens_per_s": 512 / dr,
+                          "sample": "8 tokens of the 4096-token prefill (Zipf bias) through the "
+                                    "whole layer, full output, extrapolated per token; the "
+                                    "router alone over 512 tokens"}
+
+        Hm, Fm, Em = 7168, 2048, 384
+        md = [synth.expert_mxfp4(0, e, Hm, Fm) for e in range(2)]
+        msh = synth.expert_mxfp4(0, -1, Hm, Fm)
+        mWr, _ = synth.router_weights(0, Em, Hm)
+        mb = synth.uniform_bias(0, Em)
+        xm = synth.activations(20, 1, Hm)
+        t0 = time.perf_counter()
+        oracle.mx_layer(xm, mWr, mb, md, msh, K_TOP, 1.0, expert_map=[e % 2 for e in range(Em)])
+        dt = time.perf_counter() - t0
+        res["mxfp4"] = {"value": 1 / dt, "unit": "tokens/s",
+                        "sample": "1 token of the 64-token MXFP4 wide-layer call, full output, "
+                                  "fp64 sums"}
+
+        L, steps = 16, args.stream_steps
+        demand, predict = synth.zipf_trace(3, L, E, K_TOP, steps)
+        t0 = time.perf_counter()
+        oracle.cache_sim(L, E, K_TOP, (24 << 30) // (gu_section_bytes(H, F, G) + dn_section_bytes(H, F, G)), demand,
+                         predict, wrap=False)
+        dt = time.perf_counter() - t0
+        res["streaming_cache_sim"] = {"value": steps / dt, "unit": "tokens/s (cache logic only)",
+                                      "sample": "the cache state machine over the %d-step, "
+                                                "16-layer trace" % steps}
+    for v in res.values():
+        v.update({"cores": 1, "kind": "oracle"})
+    return res
 
 
 def main():
@@ -471,7 +697,7 @@ def main():
                     help="distinct synthetic experts copied into the 256 device blobs")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-steps-max", type=int, default=40)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-small-batches", action="store_true",
@@ -482,6 +708,7 @@ def main():
                     help="also run one device-to-device copy of this many MiB (HBM counter "
                          "calibration under rocprofv3 --pmc)")
     ap.add_argument("--no-mx", action="store_true")
+    ap.add_argument("--no-tiny", action="store_true", help="skip the tiny 16-token layer line")
     ap.add_argument("--no-stream", action="store_true")
     ap.add_argument("--stream-steps", type=int, default=96)
     ap.add_argument("--stream-phys", type=int, default=48)
@@ -519,10 +746,14 @@ def main():
     # read, the per-slot projections and the output written (down)
     gu_bytes = K_TOP * gu_section_bytes(H, F, G) + H + K_TOP * F * 4
     gu_us = res["kernels_us"]["gateup"]
-    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
     S = K_TOP + 1
     dn_bytes = S * dn_section_bytes(H, F, G) + S * F * 4 + S * H * 4 + H * 4
     dn_us = res["kernels_us"]["down"]
+    # the decode GEMV projections of a step: routed gate/up + every down
+    gemv_bytes = gu_bytes + dn_bytes
+    gemv_us = gu_us + dn_us
+    achieved = gemv_bytes / (gemv_us * 1e-6) / 1e9
+    traffic = measured_traffic()
     layer_bytes = S * (gu_section_bytes(H, F, G) + dn_section_bytes(H, F, G)) + E * H * 4
     line = {
         "metric": METRIC,
@@ -547,18 +778,27 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gateup_bs1_kernel (gate/up projections + SwiGLU of the 8 routed experts)",
+            "kernel": "decode GEMV projections: gateup_bs1_kernel (routed gate/up + SwiGLU) "
+                      "and down_bs1h_kernel (requant, 9 down projections, combine)",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(),
-            "bytes_per_launch": gu_bytes,
-            "avg_us": gu_us,
+            "traffic": (traffic["gateup"] + traffic["down"]) if traffic else None,
+            "bytes_per_step": gemv_bytes,
+            "avg_us": gemv_us,
+            "per_kernel": {
+                "gateup": {"bytes_per_launch": gu_bytes, "avg_us": gu_us,
+                           "achieved": gu_bytes / (gu_us * 1e-6) / 1e9,
+                           "frac": gu_bytes / (gu_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                           "traffic": traffic["gateup"] if traffic else None},
+                "down": {"bytes_per_launch": dn_bytes, "avg_us": dn_us,
+                         "achieved": dn_bytes / (dn_us * 1e-6) / 1e9,
+                         "frac": dn_bytes / (dn_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": traffic["down"] if traffic else None},
+            },
         },
-        "gemv_hbm": {
-            "down_achieved_GBs": dn_bytes / (dn_us * 1e-6) / 1e9,
-            "down_bytes_per_launch": dn_bytes,
+        "layer_hbm": {
             # every weight byte of the step (9 experts + router) over the step time
             "layer_bytes_per_step": layer_bytes,
             "layer_GBs": layer_bytes / (ms_per_step * 1e-3) / 1e9,
@@ -572,6 +812,11 @@ def main():
     }
     if not args.no_small_batches:
         line["decode_small_batches"] = run_small_batches(args, lay)
+    tiny = None
+    if not args.no_tiny:
+        tiny = build_tiny(args)
+        line["tiny"] = run_tiny(args, tiny[0])
+        tiny[0].close()
     if not args.no_prefill:
         line["prefill"] = run_prefill(args, lay)
     if not args.no_stream:
@@ -580,6 +825,8 @@ def main():
         line["mxfp4"] = run_mx(args)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args, lay, W)
+        if tiny is not None:
+            line["cpu_baseline_other_workloads"] = cpu_baselines_other(args, W, tiny[1])
     else:
         line["cpu_baseline"] = None
     line["host"] = platform.node()

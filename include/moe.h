@@ -51,7 +51,7 @@ typedef int32_t moe_status;
 
 /* Shape and numerics of one MoE layer.
  *  hidden H, ffn F: multiples of 256.  n_experts E in [1, 1024].
- *  top_k k in [1, min(E, 16)].  n_shared in {0, 1}.
+ *  top_k k in [1, min(E, 32)].  n_shared in {0, 1}.
  *  group: 32 or 64 for INT4 (inputs per fp16 scale), 32 for MXFP4.
  *  routed_scale r: multiplies the normalised routed gate weights.
  *  out_dtype: MOE_DT_F32 or MOE_DT_BF16 (round to nearest even of the fp32). */
@@ -225,6 +225,11 @@ typedef struct moe_cache_desc {
     int32_t backend;
 } moe_cache_desc;
 
+/* Counters since creation or the last reset.  copy_busy_ms: the summed
+ * durations of the host-to-device copies (HIP backend; the copy stream runs
+ * them one at a time, so this is the copy engine's busy time), timed by event
+ * pairs around each copy; copies_timed: how many.  moe_cache_stats_get waits
+ * for the copies issued so far to finish before it reads them. */
 typedef struct moe_cache_stats {
     int64_t demand_hits, demand_misses;
     int64_t prefetch_issued, prefetch_used, prefetch_wasted, prefetch_skipped;
@@ -232,6 +237,8 @@ typedef struct moe_cache_stats {
     int64_t evictions;
     int64_t bytes_copied;
     int64_t n_slots;
+    double copy_busy_ms;
+    int64_t copies_timed;
 } moe_cache_stats;
 
 /* One logical cache event (kind: 0 hit, 1 miss, 2 prefetch issued, 3 prefetch

@@ -51,7 +51,8 @@ class moe_cache_desc(C.Structure):
 class moe_cache_stats(C.Structure):
     _fields_ = [(n, C.c_int64) for n in (
         "demand_hits", "demand_misses", "prefetch_issued", "prefetch_used", "prefetch_wasted",
-        "prefetch_skipped", "prefetch_resident", "evictions", "bytes_copied", "n_slots")]
+        "prefetch_skipped", "prefetch_resident", "evictions", "bytes_copied", "n_slots")] + [
+        ("copy_busy_ms", C.c_double), ("copies_timed", C.c_int64)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

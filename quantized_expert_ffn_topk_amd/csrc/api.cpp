@@ -15,17 +15,16 @@ using namespace moe;
 // ---------------------------------------------------------------------------
 // errors
 // ---------------------------------------------------------------------------
-static thread_local std::string g_last_error;
+// a fixed buffer: reporting an error allocates nothing
+static thread_local char g_last_error[512];
 
 namespace moe {
 moe_status fail(moe_status st, const char *fmt, ...)
 {
-    char buf[512];
     va_list ap;
     va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
     va_end(ap);
-    g_last_error = buf;
     return st;
 }
 
@@ -44,8 +43,8 @@ moe_status validate_desc(const moe_layer_desc *d)
         return fail(MOE_E_INVAL, "ffn=%d must be a positive multiple of 256", d->ffn);
     if (d->n_experts < 1 || d->n_experts > 1024)
         return fail(MOE_E_INVAL, "n_experts=%d must be in [1,1024]", d->n_experts);
-    if (d->top_k < 1 || d->top_k > 16 || d->top_k > d->n_experts)
-        return fail(MOE_E_INVAL, "top_k=%d must be in [1, min(n_experts,16)]", d->top_k);
+    if (d->top_k < 1 || d->top_k > 32 || d->top_k > d->n_experts)
+        return fail(MOE_E_INVAL, "top_k=%d must be in [1, min(n_experts,32)]", d->top_k);
     if (d->n_shared != 0 && d->n_shared != 1)
         return fail(MOE_E_INVAL, "n_shared=%d must be 0 or 1", d->n_shared);
     if (d->wfmt == MOE_WFMT_INT4) {
@@ -68,25 +67,23 @@ moe_status validate_desc(const moe_layer_desc *d)
 
 extern "C" const char *moe_last_error(void)
 {
-    return g_last_error.c_str();
+    return g_last_error;
 }
 
 // ---------------------------------------------------------------------------
 // context
 // ---------------------------------------------------------------------------
 
-template <class T>
-static moe_status ws_alloc(moe_ctx *c, T **p, size_t count)
+static moe_status ws_alloc(moe_ctx *c, void **p, size_t bytes)
 {
     void *q = nullptr;
-    size_t bytes = count * sizeof(T);
     if (bytes == 0)
         bytes = 16;
     hipError_t e = hipMalloc(&q, bytes);
     if (e != hipSuccess)
         return fail(MOE_E_NOMEM, "hipMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
     c->allocs.push_back(q);
-    *p = static_cast<T *>(q);
+    *p = q;
     return MOE_OK;
 }
 
@@ -149,46 +146,12 @@ extern "C" moe_status moe_ctx_create(int32_t device, const moe_layer_desc *desc,
     c->max_tokens = max_tokens;
     c->L = blob_layout(desc->hidden, desc->ffn, desc->group, desc->wfmt);
     c->S = desc->top_k + desc->n_shared;
-    const size_t T = (size_t)max_tokens, H = desc->hidden, F = desc->ffn, E = desc->n_experts;
-    const size_t k = desc->top_k, S = c->S;
-#define ALLOC(p, n)                  \
-    do {                             \
-        st = ws_alloc(c, &(p), (n)); \
-        if (st) {                    \
-            ctx_free(c);             \
-            return st;               \
-        }                            \
-    } while (0)
-    ALLOC(c->xq, T * H);
-    ALLOC(c->sa, T);
-    ALLOC(c->logits, 2 * T * E);          // two K parts for few tokens
-    ALLOC(c->idx, T * k);
-    ALLOC(c->gw, T * k);
-    ALLOC(c->cnt, E + 1);
-    ALLOC(c->list, (E + 1) * T);
-    ALLOC(c->active, E + 1);
-    ALLOC(c->n_active, 1);
-    ALLOC(c->done, 4);
-    ALLOC(c->ctr_gu, E + 1);
-    ALLOC(c->ctr_dn, H / 32);
-    ALLOC(c->h, T * S * F);
-    ALLOC(c->qh, T * S * F);
-    ALLOC(c->sh, T * S);
-    ALLOC(c->Y, T * S * H);
-    ALLOC(c->sel, k);
-    ALLOC(c->cs, 2 * E);
-    ALLOC(c->ident, T);
-    ALLOC(c->zero1, 1);
-    ALLOC(c->one1, 1);
-    ALLOC(c->dbg_cnt, 1);
-    c->max_tiles = (int)(desc->wfmt == MOE_WFMT_MXFP4
-                             ? mx_max_tiles((int)T, (int)E, desc->n_shared, (int)S)
-                             : mfma_max_tiles((int)T, (int)E, desc->n_shared));
-    ALLOC(c->tiles, (size_t)c->max_tiles * 2);
-    ALLOC(c->n_tiles, 4);
-    if (desc->wfmt == MOE_WFMT_MXFP4)
-        ALLOC(c->hb, T * S * F);
-#undef ALLOC
+    st = ws_plan(c, [c](void **p, size_t bytes, int) { return ws_alloc(c, p, bytes); });
+    if (st) {
+        ctx_free(c);
+        return st;
+    }
+    const size_t T = (size_t)max_tokens, H = desc->hidden, E = desc->n_experts;
     std::vector<int32_t> ident(T);
     for (size_t i = 0; i < T; ++i)
         ident[i] = (int32_t)i;
@@ -371,8 +334,9 @@ static bool small_path(const moe_ctx *c, int T)
 {
     // the fused down kernel requantises SwiGLU rows of up to 4096 values
     // (the fused kernels keep a token's router slice and a SwiGLU row in registers)
+    // (and at most 16 ranks: the fused routing launch keeps 16 candidates)
     return T == 1 && c->d.wfmt == MOE_WFMT_INT4 && c->d.ffn <= 4096 &&
-           c->d.hidden <= 8192 && !use_mfma(c, T);
+           c->d.hidden <= 8192 && c->d.top_k <= 16 && !use_mfma(c, T);
 }
 
 // One token: expert FFN straight from the top-k output (kernels_bs1.hip).
@@ -665,6 +629,16 @@ extern "C" moe_status moe_layer_forward(moe_ctx *ctx, const void *x, int32_t T,
     moe_status s = check_call(ctx, x, T, w);
     if (s)
         return s;
+    return layer_forward_enqueue(ctx, x, T, w, cache, layer, idx_out, gate_w_out, out,
+                                 static_cast<hipStream_t>(stream));
+}
+
+moe_status moe::layer_forward_enqueue(moe_ctx *ctx, const void *x, int32_t T,
+                                      const moe_layer_weights *w, moe_cache *cache,
+                                      int32_t layer, int32_t *idx_out, float *gate_w_out,
+                                      void *out, hipStream_t st)
+{
+    moe_status s = MOE_OK;
     if (T == 0)
         return MOE_OK;
     if (!out)
@@ -680,7 +654,6 @@ extern "C" moe_status moe_layer_forward(moe_ctx *ctx, const void *x, int32_t T,
         return fail(MOE_E_INVAL, "shared expert blob is NULL");
     if (!cache && !w->expert_ptrs)
         return fail(MOE_E_INVAL, "expert_ptrs is NULL");
-    hipStream_t st = static_cast<hipStream_t>(stream);
     int32_t *idx = idx_out ? idx_out : ctx->idx;
     float *gw = gate_w_out ? gate_w_out : ctx->gw;
     ctx->last_T = T;

@@ -56,7 +56,37 @@ struct moe_cache {
     std::vector<const void *> table_host; // [L*E] (host backend)
     int32_t *ids_pinned = nullptr;        // routing ids copied back from the device
     int ids_cap = 0;
+    // copy timing (HIP backend): a ring of (start, stop) event pairs around
+    // the host-to-device copies; copies [cp_tail, cp_head) are recorded and
+    // not yet added up.  The copy stream runs one copy at a time, so the sum
+    // of the durations is the time the copy engine was busy with them.
+    static constexpr int CP_RING = 512;
+    std::vector<hipEvent_t> cp_ev;        // [CP_RING][2]
+    mutable int64_t cp_head = 0, cp_tail = 0;
+    mutable double copy_ms = 0.0;
+    mutable int64_t copies_timed = 0;
+    mutable hipError_t cp_err = hipSuccess;
 };
+
+// waits for the recorded copies (all, or down to `keep` outstanding) and adds
+// up their durations
+static void copy_timing_drain(const moe_cache *c, int64_t keep)
+{
+    for (; c->cp_head - c->cp_tail > keep; ++c->cp_tail) {
+        const size_t i = (size_t)(c->cp_tail % moe_cache::CP_RING) * 2;
+        float ms = 0.0f;
+        hipError_t e = hipEventSynchronize(c->cp_ev[i + 1]);
+        if (e == hipSuccess)
+            e = hipEventElapsedTime(&ms, c->cp_ev[i], c->cp_ev[i + 1]);
+        if (e != hipSuccess) {
+            if (c->cp_err == hipSuccess)
+                c->cp_err = e;
+            continue;
+        }
+        c->copy_ms += ms;
+        c->copies_timed += 1;
+    }
+}
 
 static int64_t key_of(const moe_cache *c, int layer, int expert)
 {
@@ -136,9 +166,17 @@ static moe_status fill(moe_cache *c, int i, int layer, int expert, int cleared_k
         hipError_t e;
         if (s.release_recorded && (e = hipStreamWaitEvent(c->copy, s.release_ev, 0)) != hipSuccess)
             return hip_fail(e, "hipStreamWaitEvent(release)");
+        if (c->cp_head - c->cp_tail >= moe_cache::CP_RING)
+            copy_timing_drain(c, moe_cache::CP_RING - 1);
+        const size_t ri = (size_t)(c->cp_head % moe_cache::CP_RING) * 2;
+        if ((e = hipEventRecord(c->cp_ev[ri], c->copy)) != hipSuccess)
+            return hip_fail(e, "hipEventRecord(copy start)");
         if ((e = hipMemcpyAsync(s.mem, src, c->d.blob_bytes, hipMemcpyHostToDevice, c->copy)) !=
             hipSuccess)
             return hip_fail(e, "hipMemcpyAsync(expert)");
+        if ((e = hipEventRecord(c->cp_ev[ri + 1], c->copy)) != hipSuccess)
+            return hip_fail(e, "hipEventRecord(copy stop)");
+        c->cp_head += 1;
         if ((e = launch_table_update(c->table_dev, (int)k, s.mem, cleared_key, c->copy)) !=
             hipSuccess)
             return hip_fail(e, "table update launch");
@@ -166,6 +204,9 @@ static void destroy(moe_cache *c)
         (void)hipSetDevice(c->d.device);
         if (c->copy)
             (void)hipStreamSynchronize(c->copy);
+        for (hipEvent_t ev : c->cp_ev)
+            if (ev)
+                (void)hipEventDestroy(ev);
         for (Slot &s : c->slots) {
             if (s.fill_ev)
                 (void)hipEventDestroy(s.fill_ev);
@@ -228,6 +269,9 @@ extern "C" moe_status moe_cache_create(const moe_cache_desc *desc, moe_cache **o
             e = hipHostMalloc(reinterpret_cast<void **>(&c->ids_pinned), c->ids_cap * 4,
                               hipHostMallocDefault);
         }
+        c->cp_ev.assign((size_t)2 * moe_cache::CP_RING, nullptr);
+        for (size_t i = 0; e == hipSuccess && i < c->cp_ev.size(); ++i)
+            e = hipEventCreate(&c->cp_ev[i]);
         for (size_t i = 0; e == hipSuccess && i < n; ++i) {
             e = hipEventCreateWithFlags(&c->slots[i].fill_ev, hipEventDisableTiming);
             if (e == hipSuccess)
@@ -407,7 +451,15 @@ extern "C" moe_status moe_cache_stats_get(const moe_cache *cache, moe_cache_stat
 {
     if (!cache || !out)
         return fail(MOE_E_INVAL, "NULL argument");
+    copy_timing_drain(cache, 0);
     *out = cache->st;
+    out->copy_busy_ms = cache->copy_ms;
+    out->copies_timed = cache->copies_timed;
+    if (cache->cp_err != hipSuccess) {
+        const hipError_t e = cache->cp_err;
+        cache->cp_err = hipSuccess;
+        return hip_fail(e, "copy timing events");
+    }
     return MOE_OK;
 }
 
@@ -415,6 +467,10 @@ extern "C" void moe_cache_reset_stats(moe_cache *cache)
 {
     if (!cache)
         return;
+    copy_timing_drain(cache, 0);
+    cache->copy_ms = 0.0;
+    cache->copies_timed = 0;
+    cache->cp_err = hipSuccess;
     int64_t n = cache->st.n_slots;
     cache->st = moe_cache_stats{};
     cache->st.n_slots = n;

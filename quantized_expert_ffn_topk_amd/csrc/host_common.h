@@ -55,6 +55,68 @@ struct moe_ctx {
 
 namespace moe {
 
+// Workspace buffers of a context.  ws_plan() calls f(&member, bytes, kind)
+// once per buffer for c->d, c->max_tokens and c->S (kind WS_COUNTER: must be
+// zero before the first call, and every kernel that uses it leaves it at zero
+// again; WS_DEBUG: used by moe_debug_project only, set up at creation).  It
+// stops at the first non-OK status f returns.
+enum { WS_DATA = 0, WS_COUNTER = 1, WS_DEBUG = 2 };
+size_t mfma_max_tiles(int T, int E, int n_shared, int S);
+size_t mx_max_tiles(int T, int E, int n_shared, int S);
+
+template <class Fn>
+moe_status ws_plan(moe_ctx *c, Fn &&f)
+{
+    const moe_layer_desc &d = c->d;
+    const size_t T = (size_t)c->max_tokens, H = d.hidden, F = d.ffn, E = d.n_experts;
+    const size_t k = d.top_k, S = c->S;
+    c->max_tiles = (int)(d.wfmt == MOE_WFMT_MXFP4
+                             ? mx_max_tiles((int)T, (int)E, d.n_shared, (int)S)
+                             : mfma_max_tiles((int)T, (int)E, d.n_shared, (int)S));
+    moe_status st = MOE_OK;
+#define WS(member, count, kind)                                                     \
+    do {                                                                            \
+        if ((st = f(reinterpret_cast<void **>(&c->member),                          \
+                    (size_t)(count) * sizeof(*c->member), (kind))) != MOE_OK)       \
+            return st;                                                              \
+    } while (0)
+    WS(done, 4, WS_COUNTER);
+    WS(ctr_gu, E + 1, WS_COUNTER);
+    WS(ctr_dn, H / 32, WS_COUNTER);
+    WS(xq, T * H, WS_DATA);
+    WS(sa, T, WS_DATA);
+    WS(logits, 2 * T * E, WS_DATA);        // two K parts for few tokens
+    WS(idx, T * k, WS_DATA);
+    WS(gw, T * k, WS_DATA);
+    WS(cnt, E + 1, WS_DATA);
+    WS(list, (E + 1) * T, WS_DATA);
+    WS(active, E + 1, WS_DATA);
+    WS(n_active, 1, WS_DATA);
+    WS(h, T * S * F, WS_DATA);
+    WS(qh, T * S * F, WS_DATA);
+    WS(sh, T * S, WS_DATA);
+    WS(Y, T * S * H, WS_DATA);
+    WS(sel, k, WS_DATA);
+    WS(cs, 2 * E, WS_DATA);
+    WS(tiles, (size_t)c->max_tiles * 2, WS_DATA);
+    WS(n_tiles, 4, WS_DATA);
+    if (d.wfmt == MOE_WFMT_MXFP4)
+        WS(hb, T * S * F, WS_DATA);
+    WS(ident, T, WS_DEBUG);
+    WS(zero1, 1, WS_DEBUG);
+    WS(one1, 1, WS_DEBUG);
+    WS(dbg_cnt, 1, WS_DEBUG);
+#undef WS
+    return st;
+}
+
+// The hot part of moe_layer_forward on a prepared context (arguments already
+// checked by check_call): router, optional cache staging, expert FFNs.
+moe_status layer_forward_enqueue(moe_ctx *ctx, const void *x, int32_t T,
+                                 const moe_layer_weights *w, moe_cache *cache, int32_t layer,
+                                 int32_t *idx_out, float *gate_w_out, void *out,
+                                 hipStream_t st);
+
 moe_status fail(moe_status st, const char *fmt, ...);
 moe_status hip_fail(hipError_t e, const char *what);
 moe_status validate_desc(const moe_layer_desc *d);
@@ -81,10 +143,8 @@ hipError_t launch_gateup_mfma(const ProjArgs &a, const moe_ctx *c, int T, int F,
                               hipStream_t st);
 hipError_t launch_proj_mfma(const ProjArgs &a, const moe_ctx *c, int T, int n_rows,
                             hipStream_t st);
-size_t mfma_max_tiles(int T, int E, int n_shared);
 
 // MXFP4 path (kernels_mx.hip)
-size_t mx_max_tiles(int T, int E, int n_shared, int S);
 moe_status mx_ffn_enqueue(moe_ctx *c, const void *x, int T, const moe_layer_weights *w,
                           const void *const *expert_ptrs, const int32_t *idx, const float *gw,
                           void *out, hipStream_t st);

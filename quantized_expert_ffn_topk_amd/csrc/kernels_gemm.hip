@@ -41,10 +41,10 @@ bool use_mfma(const moe_ctx *c, int T)
     return T >= 64;
 }
 
-size_t mfma_max_tiles(int T, int E, int n_shared)
+size_t mfma_max_tiles(int T, int E, int n_shared, int S)
 {
     // every expert with rows adds at most one partial tile
-    return (size_t)T * 17 / MT + 1 + (size_t)E + (size_t)n_shared;
+    return (size_t)T * S / MT + 1 + (size_t)E + (size_t)n_shared;
 }
 
 static int tiles_bound(const moe_ctx *c, int T)

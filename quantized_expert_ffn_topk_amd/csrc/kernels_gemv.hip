@@ -547,8 +547,10 @@ hipError_t launch_combine(const float *Y, const int32_t *idx, const float *w, in
     dim3 grid((H + 255) / 256, T);
     if (k + n_shared <= 9)
         launch(combine_kernel<9>, grid, 256, 0, st, Y, idx, w, k, E, n_shared, H, out, out_dtype);
-    else
+    else if (k + n_shared <= 17)
         launch(combine_kernel<17>, grid, 256, 0, st, Y, idx, w, k, E, n_shared, H, out, out_dtype);
+    else
+        launch(combine_kernel<33>, grid, 256, 0, st, Y, idx, w, k, E, n_shared, H, out, out_dtype);
     return hipGetLastError();
 }
 

@@ -283,7 +283,7 @@ hipError_t launch_router_logits(const uint16_t *x, int T, int H, const float *Wr
 // the bitonic selection of the one-token path (lowest index first on ties).
 // With xq set the block also quantises token t (the rule of
 // quant_tokens_kernel), its row loads issued before the selection.
-template <int NW>
+template <int NW, int KEEP>
 __global__ __launch_bounds__(64 * NW) void topk_block_kernel(double *__restrict__ logits,
                                                              const float *__restrict__ bias, int E,
                                                              int k, float r, int32_t *__restrict__ idx,
@@ -294,8 +294,8 @@ __global__ __launch_bounds__(64 * NW) void topk_block_kernel(double *__restrict_
 {
     constexpr int NT = 64 * NW;
     constexpr int XL = 8192 / (8 * NT);          // 16-byte pieces per thread, H <= 8192
-    __shared__ double s_s[64 * NW], cand_c[16 * NW], sel_s[16];
-    __shared__ int cand_i[16 * NW], s_idx[16];
+    __shared__ double s_s[64 * NW], cand_c[KEEP * NW], sel_s[KEEP];
+    __shared__ int cand_i[KEEP * NW], s_idx[KEEP];
     __shared__ float s_am[NW];
     const int t = blockIdx.x, tid = threadIdx.x;
     uint4 xv[XL];
@@ -319,8 +319,8 @@ __global__ __launch_bounds__(64 * NW) void topk_block_kernel(double *__restrict_
         c = (cv != cv) ? -INFINITY : cv;
         ci = tid;
     }
-    topk_select_waves<NW>(c, ci, s_s, k, r, idx + (size_t)t * k, w + (size_t)t * k, s_idx, cand_c,
-                          cand_i, sel_s);
+    topk_select_waves<NW, KEEP>(c, ci, s_s, k, r, idx + (size_t)t * k, w + (size_t)t * k, s_idx,
+                                cand_c, cand_i, sel_s);
     if (!xq)
         return;
     float amax = 0.0f;
@@ -365,22 +365,33 @@ __global__ __launch_bounds__(64 * NW) void topk_block_kernel(double *__restrict_
         sa[t] = sc;
 }
 
+template <int KEEP>
+static void launch_topk_keep(double *logits, const float *bias, int T, int E, int k, float r,
+                             int32_t *idx, float *w, hipStream_t st, const uint16_t *x, int H,
+                             int8_t *xq, float *sa, int kparts)
+{
+    if (E <= 256)
+        launch(topk_block_kernel<4, KEEP>, T, 256, 0, st, logits, bias, E, k, r, idx, w, x, H, xq,
+               sa, kparts);
+    else if (E <= 512)
+        launch(topk_block_kernel<8, KEEP>, T, 512, 0, st, logits, bias, E, k, r, idx, w, x, H, xq,
+               sa, kparts);
+    else
+        launch(topk_block_kernel<16, KEEP>, T, 1024, 0, st, logits, bias, E, k, r, idx, w, x, H, xq,
+               sa, kparts);
+}
+
 hipError_t launch_topk(double *logits, const float *bias, int T, int E, int k, float r,
                        int32_t *idx, float *w, hipStream_t st, const uint16_t *x, int H,
                        int8_t *xq, float *sa, int kparts)
 {
     if (T <= 0)
         return hipSuccess;
-    // E <= 1024 and k <= 16 (checked at context creation)
-    if (E <= 256)
-        launch(topk_block_kernel<4>, T, 256, 0, st, logits, bias, E, k, r, idx, w, x, H, xq, sa,
-               kparts);
-    else if (E <= 512)
-        launch(topk_block_kernel<8>, T, 512, 0, st, logits, bias, E, k, r, idx, w, x, H, xq, sa,
-               kparts);
+    // E <= 1024 and k <= 32 (checked at context creation)
+    if (k <= 16)
+        launch_topk_keep<16>(logits, bias, T, E, k, r, idx, w, st, x, H, xq, sa, kparts);
     else
-        launch(topk_block_kernel<16>, T, 1024, 0, st, logits, bias, E, k, r, idx, w, x, H, xq, sa,
-               kparts);
+        launch_topk_keep<32>(logits, bias, T, E, k, r, idx, w, st, x, H, xq, sa, kparts);
     return hipGetLastError();
 }
 

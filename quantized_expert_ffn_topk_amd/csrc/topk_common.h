@@ -64,31 +64,34 @@ __device__ __forceinline__ void wave_sort_sel(double &c, int &ci)
     sort_step<64, 1>(c, ci);
 }
 
-// Top-k of one token for E <= 64*NW (NW = 4, 8 or 16 waves), k <= 16.
-// Thread e < E holds the biased score c of expert e (NaN already mapped to
-// -inf) and has put its sigmoid score in s_s[e]; other threads hold (-inf,
-// INT_MAX).  Each wave sorts its 64 candidates and keeps the first 16; while
-// more than 64 remain, waves sort them again 64 at a time; wave 0 sorts the
-// last at most 64.  The order is total, so the grouping does not change the
-// result.  Writes the ranks' ids (s_idx too) and weights w_i = s_i / sum(s) *
-// r, the sum taken in rank order in fp64.  cand_c/cand_i hold 16*NW entries.
-template <int NW>
+// Top-k of one token for E <= 64*NW (NW = 4, 8 or 16 waves), k <= KEEP (16 or
+// 32).  Thread e < E holds the biased score c of expert e (NaN already mapped
+// to -inf) and has put its sigmoid score in s_s[e]; other threads hold (-inf,
+// INT_MAX).  Each wave sorts its 64 candidates and keeps the first KEEP; while
+// more than 64 remain, waves sort them again 64 at a time and keep KEEP of
+// each 64; wave 0 sorts the last at most 64.  Every group of 64 keeps all of
+// its members that belong to the global top k (k <= KEEP), and the order is
+// total, so the grouping does not change the result.  Writes the ranks' ids
+// (s_idx too) and weights w_i = s_i / sum(s) * r, the sum taken in rank order
+// in fp64.  cand_c/cand_i hold KEEP*NW entries, s_idx and sel_s KEEP.
+template <int NW, int KEEP>
 __device__ __forceinline__ void topk_select_waves(double c, int ci, const double *s_s, int k,
                                                   float r, int32_t *__restrict__ idx_out,
                                                   float *__restrict__ w_out, int32_t *s_idx,
                                                   double *cand_c, int *cand_i, double *sel_s)
 {
+    static_assert(KEEP == 16 || KEEP == 32, "a wave keeps 16 or 32 candidates");
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     wave_sort_sel(c, ci);                            // s_s is read after the next barrier
-    if (lane < 16) {
-        cand_c[wave * 16 + lane] = c;
-        cand_i[wave * 16 + lane] = ci;
+    if (lane < KEEP) {
+        cand_c[wave * KEEP + lane] = c;
+        cand_i[wave * KEEP + lane] = ci;
     }
     __syncthreads();
-    constexpr int N1 = 16 * NW;                      // 64, 128 or 256 candidates
-    constexpr int N2 = N1 > 64 ? N1 / 4 : N1;        // after one more round: <= 64
-    if (N1 > 64) {
-        constexpr int nw = N1 / 64;
+    // candidates left: KEEP*NW, then KEEP per 64 of them per round
+#pragma unroll
+    for (int n = KEEP * NW; n > 64; n = n / 64 * KEEP) {
+        const int nw = n / 64;
         double cc = -INFINITY;
         int cci = INT_MAX;
         if (wave < nw) {
@@ -97,15 +100,21 @@ __device__ __forceinline__ void topk_select_waves(double c, int ci, const double
             wave_sort_sel(cc, cci);
         }
         __syncthreads();
-        if (wave < nw && lane < 16) {
-            cand_c[16 * wave + lane] = cc;
-            cand_i[16 * wave + lane] = cci;
+        if (wave < nw && lane < KEEP) {
+            cand_c[KEEP * wave + lane] = cc;
+            cand_i[KEEP * wave + lane] = cci;
         }
         __syncthreads();
     }
+    constexpr int NL = [] {
+        int n = KEEP * NW;
+        while (n > 64)
+            n = n / 64 * KEEP;
+        return n;
+    }();                                             // at most 64 candidates left
     if (wave == 0) {
-        c = lane < N2 ? cand_c[lane] : -INFINITY;
-        ci = lane < N2 ? cand_i[lane] : INT_MAX;
+        c = lane < NL ? cand_c[lane] : -INFINITY;
+        ci = lane < NL ? cand_i[lane] : INT_MAX;
         wave_sort_sel(c, ci);
         if (lane < k) {
             s_idx[lane] = ci;
@@ -130,7 +139,7 @@ __device__ __forceinline__ void topk_select_256(double c, int ci, const double *
                                                 float *__restrict__ w_out, int32_t *s_idx,
                                                 double *cand_c, int *cand_i, double *sel_s)
 {
-    topk_select_waves<4>(c, ci, s_s, k, r, idx_out, w_out, s_idx, cand_c, cand_i, sel_s);
+    topk_select_waves<4, 16>(c, ci, s_s, k, r, idx_out, w_out, s_idx, cand_c, cand_i, sel_s);
 }
 
 }  // namespace moe

@@ -51,7 +51,7 @@ def test_blob_bytes_match_page_figures():
 
 @pytest.mark.parametrize("field,val", [
     ("hidden", 100), ("ffn", 0), ("n_experts", 0), ("n_experts", 2000), ("top_k", 0),
-    ("top_k", 17), ("n_shared", 2), ("group", 16), ("wfmt", 7), ("out_dtype", 5)])
+    ("top_k", 33), ("n_shared", 2), ("group", 16), ("wfmt", 7), ("out_dtype", 5)])
 def test_invalid_desc_rejected_before_any_gpu_call(field, val):
     d = make_desc(256, 256, 8, 2, 1)
     setattr(d, field, val)

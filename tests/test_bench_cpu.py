@@ -46,8 +46,9 @@ def test_section_bytes_add_up_to_the_blob(g):
 def test_counter_record_parses():
     text = open(bench.TRAFFIC_RECORD).read()
     rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
-    assert rec["kernel"] == "gateup_bs1_kernel"
-    assert rec["traffic_bytes_per_launch"] > 0
+    assert rec["kernel"] == "gateup_bs1_kernel, down_bs1h_kernel"
+    assert rec["traffic_bytes_per_launch"]["gateup"] > 0
+    assert rec["traffic_bytes_per_launch"]["down"] > 0
     for path in rec["sources_sha256"]:
         assert os.path.exists(os.path.join(ROOT, path)), path
     t = bench.measured_traffic()

@@ -105,6 +105,9 @@ def test_cached_layers_equal_resident_layers_and_oracle_log(n_slots, with_pred):
     for key in st:
         assert stats[key] == st[key], key
     assert stats["bytes_copied"] == stk.blob * (stats["demand_misses"] + stats["prefetch_issued"])
+    # every copy was timed, and the copy engine's busy time is positive
+    assert stats["copies_timed"] == stats["demand_misses"] + stats["prefetch_issued"]
+    assert stats["copy_busy_ms"] > 0.0
 
 
 def _project(ctx, blob, q):
