@@ -174,6 +174,31 @@ moe_status moe_layer_forward(moe_ctx *ctx, const void *x, int32_t T,
                              int32_t layer, int32_t *idx_out, float *gate_w_out,
                              void *out, void *stream);
 
+/* ---- whole layer without allocation ------------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, hosts that forbid hipMalloc.
+ * moe_layer_forward_noalloc computes exactly what moe_layer_forward computes
+ * with cache == NULL and the automatic kernel path (same kernels, same bits),
+ * but takes no context: desc is passed per call, and the workspace is one
+ * static device array of MOE_NOALLOC_SCRATCH_BYTES per GPU, which the library
+ * holds on each GPU it runs on until the process ends.  It runs on the
+ * current device.  It calls no hipMalloc/hipFree and allocates no host
+ * memory; its first call on a device looks up that GPU's copy of the array.
+ * x, w, idx_out (may be NULL), gate_w_out (may be NULL) and out are as for
+ * moe_layer_forward.  Errors: E_INVAL (bad desc or arguments, or a call whose
+ * workspace for T tokens at this shape exceeds the array -- e.g. more than
+ * ~40 tokens of a hidden 6144, top-8 + shared layer -- nothing is enqueued
+ * then), E_UNSUPPORTED (not a gfx950 device), E_HIP.
+ * Every call on one GPU shares that GPU's array and leaves its contents for
+ * the next: calls that overlap in time on one GPU (different streams without
+ * ordering, or several host threads) race and give wrong results; order them
+ * on one stream or synchronise them.  The call's first kernel clears the
+ * array's counters. */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)
+moe_status moe_layer_forward_noalloc(const moe_layer_desc *desc, const void *x, int32_t T,
+                                     const moe_layer_weights *w, int32_t *idx_out,
+                                     float *gate_w_out, void *out, void *stream);
+
 /* ---- expert cache ---------------------------------------------------------------
  * Source: "Guide Complet de Colibri", sections "Qu'est-ce que Colibri ?" (LRU
  * expert cache, experts loaded on demand) and "Router-Lookahead prefetch" (the

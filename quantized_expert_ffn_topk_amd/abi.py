@@ -20,6 +20,7 @@ PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
 CACHE_GLOBAL_LRU, CACHE_PER_LAYER_LRU = 0, 1
 CACHE_BACKEND_HIP, CACHE_BACKEND_HOST = 0, 1
 STAGE_DEMAND, STAGE_PREFETCH = 0, 1
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
 
 _NAMES = {OK: "OK", E_INVAL: "E_INVAL", E_UNSUPPORTED: "E_UNSUPPORTED", E_NOMEM: "E_NOMEM",
           E_HIP: "E_HIP", E_CAPACITY: "E_CAPACITY"}
@@ -94,6 +95,8 @@ def _declare(L):
         "moe_router_topk": (st, [vp, vp, i32, P(moe_layer_weights), vp, vp, vp]),
         "moe_expert_ffn": (st, [vp, vp, i32, P(moe_layer_weights), vp, vp, vp, vp]),
         "moe_layer_forward": (st, [vp, vp, i32, P(moe_layer_weights), vp, i32, vp, vp, vp, vp]),
+        "moe_layer_forward_noalloc": (st, [P(moe_layer_desc), vp, i32, P(moe_layer_weights), vp,
+                                           vp, vp, vp]),
         "moe_cache_create": (st, [P(moe_cache_desc), P(vp)]),
         "moe_cache_destroy": (None, [vp]),
         "moe_cache_stage": (st, [vp, i32, vp, i32, i32, vp, vp]),
@@ -217,6 +220,12 @@ def moe_layer_forward(ctx, x, T, weights, cache, layer, idx_out, gate_w_out, out
     check(lib().moe_layer_forward(ctx, addr(x), T, C.byref(weights), cache, layer,
                                   addr(idx_out), addr(gate_w_out), addr(out),
                                   stream_handle(stream)))
+
+
+def moe_layer_forward_noalloc(desc, x, T, weights, idx_out, gate_w_out, out, stream=None):
+    check(lib().moe_layer_forward_noalloc(C.byref(desc), addr(x), T, C.byref(weights),
+                                          addr(idx_out), addr(gate_w_out), addr(out),
+                                          stream_handle(stream)))
 
 
 def moe_cache_create(desc):
