@@ -70,15 +70,15 @@ def measured_traffic():
         return None
 
 
-def build_layer(args):
+def build_layer(args, group=G):
     from quantized_expert_ffn_topk_amd import abi, synth
     from quantized_expert_ffn_topk_amd.layer import Layer, make_desc
     t0 = time.time()
     D = args.distinct
-    distinct = [synth.expert_int4(0, e, H, F, G) for e in range(D)]
-    shared = synth.expert_int4(0, -1, H, F, G)
+    distinct = [synth.expert_int4(0, e, H, F, group) for e in range(D)]
+    shared = synth.expert_int4(0, -1, H, F, group)
     Wr, b = synth.router_weights(0, E, H)
-    desc = make_desc(H, F, E, K_TOP, 1, G, R_SCALE)
+    desc = make_desc(H, F, E, K_TOP, 1, group, R_SCALE)
     lay = Layer(desc, Wr, b, distinct, shared, [e % D for e in range(E)], max_tokens=1)
     log("layer built in %.1f s (%d distinct synthetic experts behind %d device blobs)" % (
         time.time() - t0, D, E))
@@ -391,6 +391,40 @@ def run_mx(args):
     }
 
 
+def decode_gemv_roofline(kus, g):
+    """Algorithmic bytes and HBM fraction of the one-token gate/up and down
+    launches (group size g)."""
+    gu = K_TOP * gu_section_bytes(H, F, g) + H + K_TOP * F * 4
+    S = K_TOP + 1
+    dn = S * dn_section_bytes(H, F, g) + S * F * 4 + S * H * 4 + H * 4
+    us = kus["gateup"] + kus["down"]
+    return {"bytes_per_step": gu + dn, "avg_us": us,
+            "achieved": (gu + dn) / (us * 1e-6) / 1e9,
+            "frac": (gu + dn) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
+def run_gs64(args):
+    """The GLM-shaped layer with group-64 scales (the container the pages
+    recommend): one-token decode and the 4096-token Zipf prefill."""
+    import types
+    lay, _ = build_layer(args, group=64)
+    sub = types.SimpleNamespace(**vars(args))
+    sub.steps, sub.warmup, sub.profile_steps = 300, 20, 0
+    res = run_decode(sub, lay)
+    best = min(res["eager_s"], res.get("graph_s", 1e30))
+    out = {
+        "workload": "the GLM-shaped layer with int4 group-64 fp16 scales: decode batch 1 and "
+                    "the 4096-token Zipf(1.1) prefill",
+        "decode_tokens_per_s": sub.steps / best,
+        "decode_kernels_us": {k: round(v, 3) for k, v in res["kernels_us"].items()},
+        "decode_gemv_hbm": decode_gemv_roofline(res["kernels_us"], 64),
+    }
+    if not args.no_prefill:
+        out["prefill"] = run_prefill(args, lay)
+    lay.close()
+    return out
+
+
 TINY = dict(T=16, H=2048, F=1024, E=64, k=8, r=1.0)
 
 
@@ -453,7 +487,8 @@ def run_stream(args, lay, W):
     """Expert streaming: 16 GLM-shaped layers whose 4096 routed experts live in
     pinned host memory behind a 24 GiB HBM cache (global LRU), decode batch 1,
     Zipf(1.1) routing with 70 % layer-to-layer correlation imposed through the
-    selection bias, successor-set lookahead prefetch of the next layer."""
+    selection bias, successor-set lookahead prefetch of the next layer; once
+    with plain LRU, once with the learned pinned hot-store."""
     import ctypes as C
     import torch
     from quantized_expert_ffn_topk_amd import abi, synth
@@ -469,9 +504,12 @@ def run_stream(args, lay, W):
         ptrs = (C.c_void_p * (L * E))(*[host + ((l * E + e) % n_phys) * blob
                                          for l in range(L) for e in range(E)])
         cap = 24 << 30
-        cache = abi.moe_cache_create(abi.moe_cache_desc(0, L, E, blob, cap, C.addressof(ptrs),
-                                                        abi.CACHE_GLOBAL_LRU, abi.CACHE_BACKEND_HIP))
         demand, predict = synth.zipf_trace(3, L, E, K_TOP, steps)
+        # an earlier session of the same routing model (same hot experts,
+        # other draws): its usage counts are what the hot-store learnt
+        hist, _ = synth.zipf_trace(4, L, E, K_TOP, 256, model_seed=3)
+        usage0 = np.bincount((np.arange(L)[None, :, None] * E + hist).ravel(),
+                             minlength=L * E).astype(np.int64)
         bias = torch.from_numpy(np.stack([[synth.forcing_bias(E, demand[t, l]) for l in range(L)]
                                           for t in range(steps)])).to(lay.dev)
         ctx = abi.moe_ctx_create(0, lay.desc, 1)
@@ -480,28 +518,48 @@ def run_stream(args, lay, W):
         stream = torch.cuda.Stream()
         sh = abi.stream_handle(stream)
 
-        def layer_call(t, l):
-            wts = abi.moe_layer_weights(lay.Wr.data_ptr(), bias[t, l].data_ptr(), None,
-                                        lay.shared_blob.data_ptr())
-            abi.moe_layer_forward(ctx, xs[t * L + l:t * L + l + 1], 1, wts, cache, l, idx, w, out, sh)
-            if l + 1 < L:
-                abi.moe_cache_stage(cache, l + 1, predict[t, l], abi.STAGE_PREFETCH, sh)
-            abi.moe_cache_release(cache, l, sh)
-
         warm = min(8, steps // 4)
-        for t in range(warm):
-            for l in range(L):
-                layer_call(t, l)
-        torch.cuda.synchronize()
-        abi.moe_cache_reset_stats(cache)
-        t0 = time.perf_counter()
-        for t in range(warm, steps):
-            for l in range(L):
-                layer_call(t, l)
-        stream.synchronize()
-        dt = time.perf_counter() - t0
-        st = abi.moe_cache_stats_get(cache)
-        abi.moe_cache_destroy(cache)
+
+        def stream_pass(n_pin):
+            """The trace through a fresh cache; n_pin > 0: the hot-store, its
+            usage loaded from the earlier session and the n_pin hottest keys
+            pinned before the first step, re-pinned from the counts so far
+            every 32 steps."""
+            cache = abi.moe_cache_create(abi.moe_cache_desc(
+                0, L, E, blob, cap, C.addressof(ptrs), abi.CACHE_GLOBAL_LRU,
+                abi.CACHE_BACKEND_HIP))
+            if n_pin:
+                abi.moe_cache_usage_set(cache, usage0)
+                abi.moe_cache_pin_hot(cache, n_pin, K_TOP)
+
+            def layer_call(t, l):
+                wts = abi.moe_layer_weights(lay.Wr.data_ptr(), bias[t, l].data_ptr(), None,
+                                            lay.shared_blob.data_ptr())
+                abi.moe_layer_forward(ctx, xs[t * L + l:t * L + l + 1], 1, wts, cache, l, idx, w,
+                                      out, sh)
+                if l + 1 < L:
+                    abi.moe_cache_stage(cache, l + 1, predict[t, l], abi.STAGE_PREFETCH, sh)
+                abi.moe_cache_release(cache, l, sh)
+
+            for t in range(warm):
+                for l in range(L):
+                    layer_call(t, l)
+            torch.cuda.synchronize()
+            abi.moe_cache_reset_stats(cache)
+            t0 = time.perf_counter()
+            for t in range(warm, steps):
+                if n_pin and t % 32 == 0:
+                    abi.moe_cache_pin_hot(cache, n_pin, K_TOP)
+                for l in range(L):
+                    layer_call(t, l)
+            stream.synchronize()
+            dt_ = time.perf_counter() - t0
+            st_ = abi.moe_cache_stats_get(cache)
+            abi.moe_cache_destroy(cache)
+            return dt_, st_
+
+        dt, st = stream_pass(0)
+        dt_hot, st_hot = stream_pass(args.stream_pins)
 
         # the same layer calls with every expert resident (the layer's own 256
         # device blobs, no cache) and the same host synchronisation on the
@@ -569,6 +627,138 @@ def run_stream(args, lay, W):
         "predictor": {"precision": hit / tot_p if tot_p else None,
                       "recall": hit / tot_a if tot_a else None},
         "misses_per_token": st["demand_misses"] / n,
+        "copies_per_token": (st["demand_misses"] + st["prefetch_issued"]) / n,
+        "stats": st,
+        "hot_store": {
+            "pinned_keys": st_hot["pinned"],
+            "usage": "counts of an earlier 256-step session of the same routing model; the "
+                     "hottest keys pinned before the run and re-pinned every 32 steps",
+            "tokens_per_s": n / dt_hot,
+            "demand_hit_rate": st_hot["demand_hits"] / (st_hot["demand_hits"] +
+                                                        st_hot["demand_misses"]),
+            "misses_per_token": st_hot["demand_misses"] / n,
+            "copies_per_token": (st_hot["demand_misses"] + st_hot["prefetch_issued"] +
+                                 st_hot["pin_fills"]) / n,
+            "h2d_GBs_copy_busy": (st_hot["bytes_copied"] / (st_hot["copy_busy_ms"] * 1e-3) / 1e9
+                                  if st_hot["copy_busy_ms"] > 0 else None),
+            "stats": st_hot,
+        },
+    }
+
+
+def run_stream_lookahead(args, lay):
+    """Expert streaming with the real router lookahead: 16 GLM-shaped layers,
+    each with its own router weights N(0, 0.02) and a Zipf(1.1)-calibrated
+    selection bias over its own expert permutation, composed as
+    x_{l+1} = bf16(x_l + gamma * y_l); the prefetch guess for layer l+1 is
+    layer l+1's router applied to x_l (moe_router_topk), issued while layer l
+    runs.  gamma is calibrated first on resident experts so that the
+    prediction's precision lands near the 71.6 % the pages report."""
+    import ctypes as C
+    import torch
+    from quantized_expert_ffn_topk_amd import abi, synth
+    L, steps = 16, args.stream_steps
+    blob = abi.moe_blob_bytes(lay.desc)
+    Wr = [torch.from_numpy(synth.router_weights(500 + l, E, H)[0]).to(lay.dev) for l in range(L)]
+    bias = [torch.from_numpy(synth.zipf_bias(600 + l, E)).to(lay.dev) for l in range(L)]
+    ctx = abi.moe_ctx_create(0, lay.desc, 1)
+    stream = torch.cuda.Stream()
+    sh = abi.stream_handle(stream)
+    idx, w, out = lay._outs(1)
+    pred = torch.empty((1, K_TOP), dtype=torch.int32, device=lay.dev)
+    pw = torch.empty((1, K_TOP), dtype=torch.float32, device=lay.dev)
+    pred_host = torch.empty((L, K_TOP), dtype=torch.int32, pin_memory=True)
+    x0 = lay.x_tensor(synth.activations(31, steps, H))
+
+    def wts(l, ptrs):
+        return abi.moe_layer_weights(Wr[l].data_ptr(), bias[l].data_ptr(), ptrs,
+                                     lay.shared_blob.data_ptr())
+
+    def step(t, gamma, cache):
+        """One token through the 16 layers; returns per layer (actual ids,
+        predicted ids for that layer or None)."""
+        x = x0[t:t + 1]
+        rec = []
+        with torch.cuda.stream(stream):
+            for l in range(L):
+                if l + 1 < L:
+                    abi.moe_router_topk(ctx, x, 1, wts(l + 1, None), pred, pw, sh)
+                    pred_host[l].copy_(pred[0], non_blocking=True)
+                abi.moe_layer_forward(ctx, x, 1, wts(l, None if cache else lay.ptrs.data_ptr()),
+                                      cache, l, idx, w, out, sh)
+                if cache is not None:
+                    if l + 1 < L:      # the router sync above made the guess visible
+                        abi.moe_cache_stage(cache, l + 1, pred_host[l].numpy(),
+                                            abi.STAGE_PREFETCH, sh)
+                    abi.moe_cache_release(cache, l, sh)
+                else:
+                    stream.synchronize()
+                rec.append(idx[0].clone())
+                x = (x.view(torch.bfloat16).float() + out * gamma).to(torch.bfloat16).view(torch.int16)
+        stream.synchronize()
+        return [r.cpu().numpy() for r in rec], pred_host.numpy().copy()
+
+    def precision(gamma, t0, n):
+        hit = 0
+        for t in range(t0, t0 + n):
+            act, pr = step(t, gamma, None)
+            hit += sum(len(set(act[l + 1].tolist()) & set(pr[l].tolist())) for l in range(L - 1))
+        return hit / (n * (L - 1) * K_TOP)
+
+    target = 0.716
+    cal = {}
+    for g in (0.05, 0.1, 0.2, 0.3, 0.5, 1.0):
+        cal[g] = precision(g, 0, 6)
+    gamma = min(cal, key=lambda g: abs(cal[g] - target))
+
+    n_phys = args.stream_phys
+    host = abi.moe_host_alloc_pinned(n_phys * blob)
+    try:
+        base = np.ctypeslib.as_array(C.cast(host, C.POINTER(C.c_uint8)), shape=(n_phys * blob,))
+        for i in range(n_phys):
+            base[i * blob:(i + 1) * blob] = lay.blobs[i % len(lay.blobs)].cpu().numpy()
+        ptrs = (C.c_void_p * (L * E))(*[host + ((l * E + e) % n_phys) * blob
+                                         for l in range(L) for e in range(E)])
+        cache = abi.moe_cache_create(abi.moe_cache_desc(0, L, E, blob, 24 << 30, C.addressof(ptrs),
+                                                        abi.CACHE_GLOBAL_LRU, abi.CACHE_BACKEND_HIP))
+        warm = min(8, steps // 4)
+        for t in range(warm):
+            step(t, gamma, cache)
+        abi.moe_cache_reset_stats(cache)
+        hit = tot = 0
+        t0 = time.perf_counter()
+        for t in range(warm, steps):
+            act, pr = step(t, gamma, cache)
+            hit += sum(len(set(act[l + 1].tolist()) & set(pr[l].tolist())) for l in range(L - 1))
+            tot += (L - 1) * K_TOP
+        dt = time.perf_counter() - t0
+        st = abi.moe_cache_stats_get(cache)
+        abi.moe_cache_destroy(cache)
+    finally:
+        abi.moe_host_free_pinned(host)
+        abi.moe_ctx_destroy(ctx)
+    n = steps - warm
+    dem = st["demand_hits"] + st["demand_misses"]
+    return {
+        "workload": "expert streaming with the router lookahead: 16 GLM-shaped layers with their "
+                    "own routers and Zipf(1.1) biases, x_(l+1) = bf16(x_l + gamma*y_l), decode "
+                    "batch 1, the guess for layer l+1 = layer l+1's router on x_l; 4096 routed "
+                    "experts in pinned host memory (keys aliased onto %d physical blobs), 24 GiB "
+                    "HBM LRU pool" % n_phys,
+        "gamma": gamma,
+        "gamma_calibration_precision": {str(g): v for g, v in cal.items()},
+        "predictor": {"precision": hit / tot, "recall": hit / tot,
+                      "note": "k guessed, k actual per layer: precision equals recall"},
+        "tokens_per_s": n / dt,
+        "ms_per_token": 1e3 * dt / n,
+        "demand_hit_rate": st["demand_hits"] / dem if dem else None,
+        "prefetch_precision": (st["prefetch_used"] / st["prefetch_issued"]
+                               if st["prefetch_issued"] else None),
+        "prefetch_coverage": (st["prefetch_used"] / (st["prefetch_used"] + st["demand_misses"])
+                              if st["prefetch_used"] + st["demand_misses"] else None),
+        "h2d_GBs_copy_busy": (st["bytes_copied"] / (st["copy_busy_ms"] * 1e-3) / 1e9
+                              if st["copy_busy_ms"] > 0 else None),
+        "copies_per_token": (st["demand_misses"] + st["prefetch_issued"]) / n,
         "stats": st,
     }
 
@@ -709,9 +899,12 @@ def main():
                          "calibration under rocprofv3 --pmc)")
     ap.add_argument("--no-mx", action="store_true")
     ap.add_argument("--no-tiny", action="store_true", help="skip the tiny 16-token layer line")
+    ap.add_argument("--no-gs64", action="store_true", help="skip the group-64 layer line")
     ap.add_argument("--no-stream", action="store_true")
     ap.add_argument("--stream-steps", type=int, default=96)
     ap.add_argument("--stream-phys", type=int, default=48)
+    ap.add_argument("--stream-pins", type=int, default=900,
+                    help="keys the hot-store pins in the second streaming pass")
     ap.add_argument("--mx-calls", type=int, default=10)
     ap.add_argument("--mx-distinct", type=int, default=4)
     args = ap.parse_args()
@@ -821,8 +1014,11 @@ def main():
         line["prefill"] = run_prefill(args, lay)
     if not args.no_stream:
         line["streaming"] = run_stream(args, lay, W)
+        line["streaming_lookahead"] = run_stream_lookahead(args, lay)
     if not args.no_mx:
         line["mxfp4"] = run_mx(args)
+    if not args.no_gs64:
+        line["gs64"] = run_gs64(args)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args, lay, W)
         if tiny is not None:

@@ -262,12 +262,14 @@ typedef struct moe_cache_stats {
     int64_t evictions;
     int64_t bytes_copied;
     int64_t n_slots;
+    int64_t pinned, pin_fills;
     double copy_busy_ms;
     int64_t copies_timed;
 } moe_cache_stats;
 
 /* One logical cache event (kind: 0 hit, 1 miss, 2 prefetch issued, 3 prefetch
- * already resident, 4 prefetch skipped, 5 eviction). */
+ * already resident, 4 prefetch skipped, 5 eviction, 6 pinned key copied in,
+ * 7 pinned key already resident). */
 typedef struct moe_cache_event {
     int32_t kind, layer, expert, slot;
 } moe_cache_event;
@@ -285,6 +287,28 @@ void moe_cache_reset_stats(moe_cache *cache);
  * written; the log is kept only when enabled. */
 moe_status moe_cache_log_enable(moe_cache *cache, int32_t on);
 int64_t moe_cache_event_log(const moe_cache *cache, moe_cache_event *out, int64_t cap);
+/* Learned pinned hot-store.  Source: aifrontierpost tutorial, introduction
+ * (measured routing heat drives the LRU cache and a learned pinned hot-store)
+ * and "Step 4 -- Run it" (the usage file records which experts the workload
+ * routes to and the hottest are pinned); kongchang article, storage-tier
+ * section (expert usage is recorded, hit rates grow with use).
+ * Every DEMAND access of key (l, e) adds one to usage[l*n_experts + e]
+ * (prefetches do not count).  moe_cache_pin_hot: between layers (no slot
+ * locked; else E_INVAL and nothing changes) unpins every slot, then takes the
+ * keys with a nonzero count by count descending, key ascending, and pins them
+ * until n are pinned: a resident key's slot as it is, a missing key copied
+ * into the LRU unlocked unpinned slot of its partition (on the copy stream,
+ * waited for by the next DEMAND of the key as any fill).  At most (partition
+ * slots - reserve) slots of a partition are pinned (reserve >= 1: pass at
+ * least the number of distinct experts one layer call demands), so a layer
+ * always finds room; keys whose partition is full are passed over.  A pinned
+ * slot is never evicted by DEMAND, PREFETCH or a later pin until the next
+ * moe_cache_pin_hot.  moe_cache_usage_get / _set copy the [n_layers *
+ * n_experts] counts out / in (host memory), so a caller can keep them across
+ * runs.  Errors: E_INVAL, E_CAPACITY, E_HIP (a failed copy). */
+moe_status moe_cache_pin_hot(moe_cache *cache, int32_t n, int32_t reserve);
+moe_status moe_cache_usage_get(const moe_cache *cache, int64_t *usage_host);
+moe_status moe_cache_usage_set(moe_cache *cache, const int64_t *usage_host);
 /* Test hook: the next copy fails as if the runtime had reported an error. */
 moe_status moe_cache_debug_fail_next_copy(moe_cache *cache);
 

@@ -48,10 +48,11 @@ class CacheEvent(C.Structure):
 class CacheStats(C.Structure):
     _fields_ = [(n, C.c_int64) for n in (
         "demand_hits", "demand_misses", "prefetch_issued", "prefetch_used",
-        "prefetch_wasted", "prefetch_skipped", "prefetch_resident", "evictions")]
+        "prefetch_wasted", "prefetch_skipped", "prefetch_resident", "evictions",
+        "pinned", "pin_fills")]
 
 
-EV_HIT, EV_MISS, EV_PF_ISSUE, EV_PF_HIT, EV_PF_SKIP, EV_EVICT = range(6)
+EV_HIT, EV_MISS, EV_PF_ISSUE, EV_PF_HIT, EV_PF_SKIP, EV_EVICT, EV_PIN_FILL, EV_PIN_KEEP = range(8)
 
 
 def _declare(L):
@@ -82,6 +83,13 @@ def _declare(L):
     L.orc_cache_sim.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32, i32,
                                 C.POINTER(CacheEvent), C.c_int64, C.POINTER(CacheStats)]
     L.orc_cache_sim.restype = C.c_int64
+    L.orc_lookahead.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp]
+    L.orc_lookahead.restype = None
+    L.orc_residual_bf16.argtypes = [i32, vp, vp, C.c_float, vp]
+    L.orc_residual_bf16.restype = None
+    L.orc_cache_sim_hot.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32, i32, vp, vp,
+                                    C.POINTER(CacheEvent), C.c_int64, C.POINTER(CacheStats), vp]
+    L.orc_cache_sim_hot.restype = C.c_int64
 
 
 def _vp(a):
@@ -314,3 +322,48 @@ def cache_sim(L, E, k, n_slots, demand, predict=None, wrap=True, per_layer=False
     out = np.frombuffer(ev, dtype=np.int32, count=4 * n).reshape(n, 4).copy()
     stats = {f: getattr(st, f) for f, _ in CacheStats._fields_}
     return out, stats
+
+
+def cache_sim_hot(L, E, k, n_slots, demand, predict=None, wrap=True, per_layer=False,
+                  usage_init=None, pin_before=None):
+    """The replay with the learned pinned hot-store.  pin_before: [steps] int32,
+    the PIN(n) done before each step (-1: none), or None.  Returns (events,
+    stats, usage [L*E] int64)."""
+    demand = _c(demand, np.int32)
+    steps = demand.shape[0]
+    pr = None if predict is None else _c(predict, np.int32)
+    ui = None if usage_init is None else _c(usage_init, np.int64)
+    pb = None if pin_before is None else _c(pin_before, np.int32)
+    cap = steps * L * k * 4 + 16 + (0 if pb is None else 2 * int(np.maximum(pb, 0).sum()))
+    ev = (CacheEvent * cap)()
+    st = CacheStats()
+    usage = np.zeros(L * E, np.int64)
+    n = lib().orc_cache_sim_hot(L, E, k, n_slots, steps, _vp(demand), _vp(pr),
+                                1 if wrap else 0, 1 if per_layer else 0, _vp(ui), _vp(pb),
+                                ev, cap, C.byref(st), _vp(usage))
+    if n < 0:
+        raise RuntimeError("cache simulation failed (capacity below k?)")
+    out = np.frombuffer(ev, dtype=np.int32, count=4 * n).reshape(n, 4).copy()
+    stats = {f: getattr(st, f) for f, _ in CacheStats._fields_}
+    return out, stats, usage
+
+
+def lookahead(x_bf16, Wr_next, b_next, k):
+    """Predicted experts [T,k] of the next layer from the current state."""
+    x_bf16 = _c(x_bf16, np.uint16)
+    Wr_next = _c(Wr_next, np.float32)
+    b_next = _c(b_next, np.float32)
+    T, H = x_bf16.shape
+    idx = np.empty((T, k), np.int32)
+    lib().orc_lookahead(T, H, Wr_next.shape[0], k, _vp(x_bf16), _vp(Wr_next), _vp(b_next),
+                        _vp(idx))
+    return idx
+
+
+def residual_bf16(x_bf16, y, gamma):
+    """bf16(fp32(x) + fp32(gamma * y)) elementwise."""
+    x_bf16 = _c(x_bf16, np.uint16)
+    y = _c(y, np.float32)
+    out = np.empty_like(x_bf16)
+    lib().orc_residual_bf16(x_bf16.size, _vp(x_bf16), _vp(y), float(gamma), _vp(out))
+    return out

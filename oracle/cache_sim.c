@@ -21,6 +21,22 @@
  *    slot the prefetch is skipped.  Prefetched slots are not locked;
  *  - a prefetched slot hit by a demand counts as used; evicted before any
  *    demand, as wasted.
+ *
+ * Learned pinned hot-store (Colibri records which experts a workload routes
+ * to and pins the hottest ones: aifrontierpost tutorial, introduction and
+ * "Step 4 -- Run it"; kongchang article, storage-tier section; openapps.pro
+ * listing, "Under The Hood"):
+ *  - every DEMAND access of a key adds one to its usage count (prefetches do
+ *    not: they are guesses, not uses);
+ *  - PIN(n), between steps (no slot locked): every pinned slot is unpinned
+ *    (it stays resident); then the keys with a nonzero count, ranked by count
+ *    descending and key (layer*E + expert) ascending, are taken in rank order
+ *    until n are pinned: a resident key's slot is pinned as it is; a missing
+ *    key takes the LRU unlocked, unpinned slot of its partition (as a demand
+ *    miss would), is filled and pinned.  A partition never pins more than its
+ *    size minus k slots, so a layer's demand always finds room; a key whose
+ *    partition is full of pins is passed over;
+ *  - a pinned slot is never a victim (demand, prefetch or pin).
  */
 #include "moe_oracle.h"
 
@@ -31,16 +47,18 @@ typedef struct {
     int64_t last_use;        /* -1 when never used */
     int32_t locked_by;       /* layer holding the lock, -1 if none */
     int32_t prefetched;
+    int32_t pinned;
 } slot_t;
 
 typedef struct {
     slot_t *slot;
-    int n_slots, L, per_layer;
+    int n_slots, L, E, k, per_layer;
     int64_t clock;
     orc_cache_event *ev;
     int64_t n_ev, ev_cap;
     int overflow;
     orc_cache_stats *st;
+    int64_t *usage;          /* [L*E] demand accesses per key */
 } sim_t;
 
 static void emit(sim_t *s, int kind, int layer, int expert, int slot)
@@ -80,7 +98,7 @@ static int find_victim(const sim_t *s, int layer)
     int lo, hi, best = -1;
     part_range(s, layer, &lo, &hi);
     for (int i = lo; i < hi; ++i) {
-        if (s->slot[i].locked_by >= 0)
+        if (s->slot[i].locked_by >= 0 || s->slot[i].pinned)
             continue;
         if (best < 0 || s->slot[i].last_use < s->slot[best].last_use)
             best = i;
@@ -105,6 +123,7 @@ static int demand(sim_t *s, int layer, const int32_t *ids, int k)
 {
     for (int j = 0; j < k; ++j) {
         int e = ids[j];
+        s->usage[(size_t)layer * s->E + e] += 1;
         int i = find_resident(s, layer, e);
         if (i >= 0) {
             emit(s, ORC_EV_HIT, layer, e, i);
@@ -163,16 +182,66 @@ static void release(sim_t *s, int layer)
             s->slot[i].locked_by = -1;
 }
 
-int64_t orc_cache_sim(int L, int E, int k, int n_slots, int n_steps,
-                      const int32_t *dem, const int32_t *pred, int wrap,
-                      int per_layer, orc_cache_event *ev, int64_t ev_cap,
-                      orc_cache_stats *st)
+/* PIN(n): unpin everything, then pin the n hottest keys (see the header). */
+static void pin_hot(sim_t *s, int n)
 {
-    (void)E;
+    const int nk = s->L * s->E;
+    for (int i = 0; i < s->n_slots; ++i)
+        s->slot[i].pinned = 0;
+    s->st->pinned = 0;
+    char *taken = (char *)calloc((size_t)nk, 1);
+    for (int r = 0; r < n; ++r) {
+        /* the next key in rank order: largest count, then lowest key */
+        int best = -1;
+        for (int key = 0; key < nk; ++key) {
+            if (taken[key] || s->usage[key] <= 0)
+                continue;
+            if (best < 0 || s->usage[key] > s->usage[best])
+                best = key;
+        }
+        if (best < 0)
+            break;
+        taken[best] = 1;
+        const int layer = best / s->E, e = best % s->E;
+        int lo, hi, n_part_pinned = 0;
+        part_range(s, layer, &lo, &hi);
+        for (int i = lo; i < hi; ++i)
+            n_part_pinned += s->slot[i].pinned;
+        if (n_part_pinned >= (hi - lo) - s->k) {
+            --r;                        /* passed over: its partition is full */
+            continue;
+        }
+        int i = find_resident(s, layer, e);
+        if (i >= 0) {
+            emit(s, ORC_EV_PIN_KEEP, layer, e, i);
+        } else {
+            i = find_victim(s, layer);
+            evict(s, i);
+            s->slot[i].layer = layer;
+            s->slot[i].expert = e;
+            s->slot[i].last_use = ++s->clock;
+            emit(s, ORC_EV_PIN_FILL, layer, e, i);
+            s->st->pin_fills++;
+        }
+        s->slot[i].pinned = 1;
+        s->st->pinned++;
+    }
+    free(taken);
+}
+
+int64_t orc_cache_sim_hot(int L, int E, int k, int n_slots, int n_steps,
+                          const int32_t *dem, const int32_t *pred, int wrap,
+                          int per_layer, const int64_t *usage_init,
+                          const int32_t *pin_before, orc_cache_event *ev, int64_t ev_cap,
+                          orc_cache_stats *st, int64_t *usage_out)
+{
     sim_t s;
     s.slot = (slot_t *)malloc(sizeof(slot_t) * (size_t)(n_slots > 0 ? n_slots : 1));
+    s.usage = (int64_t *)calloc((size_t)L * (size_t)E, sizeof(int64_t));
     s.n_slots = n_slots;
     s.L = L;
+    s.E = E;
+    s.k = k;
     s.per_layer = per_layer;
     s.clock = 0;
     s.ev = ev;
@@ -183,14 +252,21 @@ int64_t orc_cache_sim(int L, int E, int k, int n_slots, int n_steps,
     st->demand_hits = st->demand_misses = 0;
     st->prefetch_issued = st->prefetch_used = st->prefetch_wasted = 0;
     st->prefetch_skipped = st->prefetch_resident = st->evictions = 0;
+    st->pinned = st->pin_fills = 0;
     for (int i = 0; i < n_slots; ++i) {
         s.slot[i].layer = s.slot[i].expert = -1;
         s.slot[i].last_use = -1;
         s.slot[i].locked_by = -1;
         s.slot[i].prefetched = 0;
+        s.slot[i].pinned = 0;
     }
+    if (usage_init)
+        for (int i = 0; i < L * E; ++i)
+            s.usage[i] = usage_init[i];
     int64_t rc = 0;
     for (int t = 0; t < n_steps && rc == 0; ++t) {
+        if (pin_before && pin_before[t] >= 0)
+            pin_hot(&s, pin_before[t]);
         for (int l = 0; l < L; ++l) {
             const int32_t *ids = dem + ((size_t)t * L + l) * k;
             if (demand(&s, l, ids, k) != 0) {
@@ -210,8 +286,21 @@ int64_t orc_cache_sim(int L, int E, int k, int n_slots, int n_steps,
             release(&s, l);
         }
     }
+    if (usage_out)
+        for (int i = 0; i < L * E; ++i)
+            usage_out[i] = s.usage[i];
     free(s.slot);
+    free(s.usage);
     if (rc != 0 || s.overflow)
         return -1;
     return s.n_ev;
+}
+
+int64_t orc_cache_sim(int L, int E, int k, int n_slots, int n_steps,
+                      const int32_t *dem, const int32_t *pred, int wrap,
+                      int per_layer, orc_cache_event *ev, int64_t ev_cap,
+                      orc_cache_stats *st)
+{
+    return orc_cache_sim_hot(L, E, k, n_slots, n_steps, dem, pred, wrap, per_layer, NULL, NULL,
+                             ev, ev_cap, st, NULL);
 }

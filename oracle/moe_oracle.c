@@ -176,6 +176,29 @@ void orc_router(int T, int H, int E, int k, float r,
 }
 
 /* ------------------------------------------------------------------------- */
+/* Router lookahead (Colibri guide, section "Router-Lookahead prefetch"): the  */
+/* next layer's router applied to the current layer's input.  The weights are */
+/* not needed for a prediction, only the selection.                           */
+/* ------------------------------------------------------------------------- */
+
+void orc_lookahead(int T, int H, int E, int k, const uint16_t *x_l, const float *Wr_next,
+                   const float *b_next, int32_t *idx_pred)
+{
+    float *w = (float *)malloc(sizeof(float) * (size_t)T * (size_t)k);
+    orc_router(T, H, E, k, 1.0f, x_l, Wr_next, b_next, idx_pred, w, NULL, NULL, NULL);
+    free(w);
+}
+
+void orc_residual_bf16(int n, const uint16_t *x, const float *y, float gamma, uint16_t *x_next)
+{
+    for (int i = 0; i < n; ++i) {
+        float t = gamma * y[i];                     /* rounded to fp32 */
+        float r = orc_bf16_to_f32(x[i]) + t;        /* rounded to fp32 */
+        x_next[i] = orc_f32_to_bf16(r);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
 /* int4 x int8 projection (the integer dot-product kernel of the Colibri      */
 /* guide, table "Points techniques cles"; group-scaled int4 of the            */
 /* aifrontierpost tutorial, "Step 3").  Inside a group the dot product is an  */

@@ -60,6 +60,21 @@ void orc_router(int T, int H, int E, int k, float r,
                 int32_t *idx, float *w,
                 double *logits, double *scores, double *choice);
 
+/* ---- router lookahead ------------------------------------------------------- */
+/* Source: "Guide Complet de Colibri", section "Router-Lookahead prefetch"
+ * (the next layer's routing is largely predictable from the current state, and
+ * a worker prefetches the predicted experts); kongchang article, storage-tier
+ * section (one-layer-ahead prefetch).  Reading: the prediction for layer l+1
+ * is layer l+1's own router applied to layer l's input x_l, before layer l's
+ * output is known: idx_pred [T,k] = the k experts with the largest
+ * sigmoid(x_l . Wr_next) + b_next, ties to the lower index, in rank order. */
+void orc_lookahead(int T, int H, int E, int k, const uint16_t *x_l, const float *Wr_next,
+                   const float *b_next, int32_t *idx_pred);
+/* The residual composition of a stack of MoE layers (reading: no norm):
+ * x_next = bf16(fp32(x) + fp32(gamma * y)) with both fp32 operations rounded
+ * to nearest and the bf16 rounding to nearest even; n elements. */
+void orc_residual_bf16(int n, const uint16_t *x, const float *y, float gamma, uint16_t *x_next);
+
 /* ---- int4 x int8 projection ---------------------------------------------------- */
 /* y[n] = fp32( fp64(sum_g acc[n,g] * S[n,g]) * s_in ),
  * acc[n,g] = sum_{k in group g} qw[n,k] * q_in[k]  (exact int32),
@@ -130,7 +145,7 @@ void orc_mx_layer(int T, int H, int F, int E, int k, float r,
 
 /* ---- expert cache state machine ------------------------------------------------------ */
 enum { ORC_EV_HIT = 0, ORC_EV_MISS = 1, ORC_EV_PF_ISSUE = 2, ORC_EV_PF_HIT = 3,
-       ORC_EV_PF_SKIP = 4, ORC_EV_EVICT = 5 };
+       ORC_EV_PF_SKIP = 4, ORC_EV_EVICT = 5, ORC_EV_PIN_FILL = 6, ORC_EV_PIN_KEEP = 7 };
 
 typedef struct orc_cache_event {
     int32_t kind, layer, expert, slot;
@@ -141,6 +156,7 @@ typedef struct orc_cache_stats {
     int64_t prefetch_issued, prefetch_used, prefetch_wasted, prefetch_skipped;
     int64_t prefetch_resident;
     int64_t evictions;
+    int64_t pinned, pin_fills;
 } orc_cache_stats;
 
 /* Replays a trace through the LRU slot pool.  For step s and layer l the
@@ -156,6 +172,20 @@ int64_t orc_cache_sim(int L, int E, int k, int n_slots, int n_steps,
                       const int32_t *demand, const int32_t *predict, int wrap,
                       int per_layer, orc_cache_event *ev, int64_t ev_cap,
                       orc_cache_stats *st);
+
+/* The same replay with the learned pinned hot-store: usage counts start from
+ * usage_init [L*E] (NULL: zeros) and count every DEMAND access; before step t
+ * with pin_before[t] >= 0 (pin_before may be NULL), PIN(pin_before[t]) unpins
+ * every slot and pins the hottest keys (count descending, key ascending, at
+ * most partition size - k per partition; missing keys are filled).  Pinned
+ * slots are never victims.  usage_out [L*E] (may be NULL) receives the final
+ * counts.  Events ORC_EV_PIN_FILL / ORC_EV_PIN_KEEP record a pinned key that
+ * was copied in / already resident. */
+int64_t orc_cache_sim_hot(int L, int E, int k, int n_slots, int n_steps,
+                          const int32_t *demand, const int32_t *predict, int wrap,
+                          int per_layer, const int64_t *usage_init,
+                          const int32_t *pin_before, orc_cache_event *ev, int64_t ev_cap,
+                          orc_cache_stats *st, int64_t *usage_out);
 
 #ifdef __cplusplus
 }

@@ -52,8 +52,8 @@ class moe_cache_desc(C.Structure):
 class moe_cache_stats(C.Structure):
     _fields_ = [(n, C.c_int64) for n in (
         "demand_hits", "demand_misses", "prefetch_issued", "prefetch_used", "prefetch_wasted",
-        "prefetch_skipped", "prefetch_resident", "evictions", "bytes_copied", "n_slots")] + [
-        ("copy_busy_ms", C.c_double), ("copies_timed", C.c_int64)]
+        "prefetch_skipped", "prefetch_resident", "evictions", "bytes_copied", "n_slots",
+        "pinned", "pin_fills")] + [("copy_busy_ms", C.c_double), ("copies_timed", C.c_int64)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -107,6 +107,9 @@ def _declare(L):
         "moe_cache_log_enable": (st, [vp, i32]),
         "moe_cache_event_log": (C.c_int64, [vp, P(moe_cache_event), C.c_int64]),
         "moe_cache_debug_fail_next_copy": (st, [vp]),
+        "moe_cache_pin_hot": (st, [vp, i32, i32]),
+        "moe_cache_usage_get": (st, [vp, vp]),
+        "moe_cache_usage_set": (st, [vp, vp]),
         "moe_host_alloc_pinned": (st, [C.c_size_t, P(vp)]),
         "moe_host_free_pinned": (st, [vp]),
         "moe_last_error": (C.c_char_p, []),
@@ -280,6 +283,23 @@ def moe_cache_event_log(cache, cap=1 << 20):
 
 def moe_cache_debug_fail_next_copy(cache):
     check(lib().moe_cache_debug_fail_next_copy(cache))
+
+
+def moe_cache_pin_hot(cache, n, reserve):
+    check(lib().moe_cache_pin_hot(cache, n, reserve))
+
+
+def moe_cache_usage_get(cache, n_keys):
+    import numpy as np
+    u = np.zeros(n_keys, np.int64)
+    check(lib().moe_cache_usage_get(cache, u.ctypes.data))
+    return u
+
+
+def moe_cache_usage_set(cache, usage):
+    import numpy as np
+    u = np.ascontiguousarray(usage, np.int64)
+    check(lib().moe_cache_usage_set(cache, u.ctypes.data))
 
 
 def moe_host_alloc_pinned(nbytes):

@@ -8,6 +8,12 @@
 // Placement decides speed only, never results (aifrontierpost tutorial,
 // "Honest limitations").
 //
+// Colibri also records which experts a workload routes to and pins the
+// hottest ones (aifrontierpost tutorial, introduction and "Step 4 -- Run it";
+// kongchang article, storage-tier section): every DEMAND access counts toward
+// its key's usage, and moe_cache_pin_hot pins the keys with the highest counts
+// in slots that are never evicted.
+//
 // Here the tiers are pinned host memory -> an HBM slot pool.  Copies run with
 // hipMemcpyAsync on the cache's own copy stream.  Each slot has a fill event
 // (recorded on the copy stream after its copy) and a release event (recorded
@@ -17,6 +23,7 @@
 // refilled while a kernel may still read it.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <unordered_map>
@@ -33,6 +40,7 @@ struct Slot {
     int64_t last_use = -1;
     int32_t locked_by = -1;
     int32_t prefetched = 0;
+    int32_t pinned = 0;
     bool fill_recorded = false, release_recorded = false;
     hipEvent_t fill_ev = nullptr, release_ev = nullptr;
     uint8_t *mem = nullptr;
@@ -45,6 +53,7 @@ struct moe_cache {
     int n_slots = 0;
     std::vector<Slot> slots;
     std::unordered_map<int64_t, int> where;
+    std::vector<int64_t> usage;           // [L*E] DEMAND accesses per key
     int64_t clock = 0;
     moe_cache_stats st{};
     bool log_on = false;
@@ -116,7 +125,7 @@ static int find_victim(const moe_cache *c, int layer)
     part_range(c, layer, &lo, &hi);
     for (int i = lo; i < hi; ++i) {
         const Slot &s = c->slots[i];
-        if (s.locked_by >= 0)
+        if (s.locked_by >= 0 || s.pinned)
             continue;
         if (best < 0 || s.last_use < c->slots[best].last_use)
             best = i;
@@ -292,6 +301,7 @@ extern "C" moe_status moe_cache_create(const moe_cache_desc *desc, moe_cache **o
             c->slots[i].mem = c->pool + i * desc->blob_bytes;
         c->table_host.assign(L * E, nullptr);
     }
+    c->usage.assign(L * E, 0);
     c->st.n_slots = (int64_t)n;
     *out = c;
     return MOE_OK;
@@ -310,7 +320,7 @@ static moe_status stage_demand(moe_cache *c, int layer, const int32_t *ids, int 
     part_range(c, layer, &lo, &hi);
     for (int i = lo; i < hi; ++i) {
         const Slot &s = c->slots[i];
-        if (s.locked_by < 0) {
+        if (s.locked_by < 0 && !s.pinned) {
             ++usable;
         } else if (s.layer == layer) {
             for (int j = 0; j < n; ++j)
@@ -324,6 +334,7 @@ static moe_status stage_demand(moe_cache *c, int layer, const int32_t *ids, int 
         return fail(MOE_E_CAPACITY, "layer %d needs %d slots, %d usable", layer, n, usable);
     for (int j = 0; j < n; ++j) {
         const int e = ids[j];
+        c->usage[(size_t)key_of(c, layer, e)] += 1;
         auto it = c->where.find(key_of(c, layer, e));
         int i;
         if (it != c->where.end()) {
@@ -393,6 +404,81 @@ static moe_status stage_prefetch(moe_cache *c, int layer, const int32_t *ids, in
         emit(c, 2, layer, e, i);
         c->st.prefetch_issued++;
     }
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_cache_pin_hot(moe_cache *c, int32_t n, int32_t reserve)
+{
+    if (!c || n < 0 || reserve < 1)
+        return fail(MOE_E_INVAL, "bad arguments");
+    for (const Slot &s : c->slots)
+        if (s.locked_by >= 0)
+            return fail(MOE_E_INVAL, "layer %d still holds slots: pin between layers",
+                        s.locked_by);
+    for (Slot &s : c->slots)
+        s.pinned = 0;
+    c->st.pinned = 0;
+    // keys with a nonzero count, count descending, key ascending
+    std::vector<int32_t> order;
+    for (size_t key = 0; key < c->usage.size(); ++key)
+        if (c->usage[key] > 0)
+            order.push_back((int32_t)key);
+    std::stable_sort(order.begin(), order.end(), [c](int32_t a, int32_t b) {
+        return c->usage[(size_t)a] > c->usage[(size_t)b];
+    });
+    int pinned = 0;
+    for (size_t r = 0; r < order.size() && pinned < n; ++r) {
+        const int key = order[r];
+        const int layer = key / c->d.n_experts, e = key % c->d.n_experts;
+        int lo, hi, part_pinned = 0;
+        part_range(c, layer, &lo, &hi);
+        for (int i = lo; i < hi; ++i)
+            part_pinned += c->slots[i].pinned;
+        if (part_pinned >= (hi - lo) - reserve)
+            continue;                       // its partition is full of pins
+        auto it = c->where.find(key);
+        int i;
+        if (it != c->where.end()) {
+            i = it->second;
+            emit(c, 7, layer, e, i);
+        } else {
+            i = find_victim(c, layer);
+            if (i < 0)
+                return fail(MOE_E_CAPACITY, "no slot left to pin (layer %d, expert %d)", layer, e);
+            int cleared;
+            evict(c, i, &cleared);
+            moe_status st = fill(c, i, layer, e, cleared);
+            if (st) {
+                c->slots[i].last_use = -1;
+                return st;
+            }
+            c->slots[i].last_use = ++c->clock;
+            emit(c, 6, layer, e, i);
+            c->st.pin_fills++;
+        }
+        c->slots[i].pinned = 1;
+        c->st.pinned++;
+        ++pinned;
+    }
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_cache_usage_get(const moe_cache *c, int64_t *usage_host)
+{
+    if (!c || !usage_host)
+        return fail(MOE_E_INVAL, "NULL argument");
+    std::copy(c->usage.begin(), c->usage.end(), usage_host);
+    return MOE_OK;
+}
+
+extern "C" moe_status moe_cache_usage_set(moe_cache *c, const int64_t *usage_host)
+{
+    if (!c || !usage_host)
+        return fail(MOE_E_INVAL, "NULL argument");
+    for (size_t i = 0; i < c->usage.size(); ++i)
+        if (usage_host[i] < 0)
+            return fail(MOE_E_INVAL, "negative usage count at key %zu", i);
+    std::copy(usage_host, usage_host + c->usage.size(), c->usage.begin());
     return MOE_OK;
 }
 
@@ -471,9 +557,10 @@ extern "C" void moe_cache_reset_stats(moe_cache *cache)
     cache->copy_ms = 0.0;
     cache->copies_timed = 0;
     cache->cp_err = hipSuccess;
-    int64_t n = cache->st.n_slots;
+    const int64_t n = cache->st.n_slots, pinned = cache->st.pinned;
     cache->st = moe_cache_stats{};
     cache->st.n_slots = n;
+    cache->st.pinned = pinned;
 }
 
 extern "C" moe_status moe_cache_log_enable(moe_cache *cache, int32_t on)

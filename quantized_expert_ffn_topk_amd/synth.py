@@ -167,16 +167,20 @@ def zipf_bias(seed, E, beta=ZIPF_BETA, s=ZIPF_S, tag="zipf"):
     return (b + noise).astype(np.float32)
 
 
-def zipf_trace(seed, L, E, k, steps, corr=0.7, s=ZIPF_S, tag="trace"):
+def zipf_trace(seed, L, E, k, steps, corr=0.7, s=ZIPF_S, tag="trace", model_seed=None):
     """Expert-streaming trace: per (step, layer) k distinct experts drawn by
     Zipf(s) rank over a per-layer seeded permutation; for layer l+1 each rank
     slot keeps, with probability corr, the successor (same Zipf rank in the
     next layer's permutation) of the expert at that rank in layer l.
+    The permutations (which experts are hot: the model) come from model_seed
+    (default: seed), the draws from seed, so two traces with one model_seed
+    and different seeds are two sessions of the same model.
     Returns (demand [steps,L,k] int32, predict [steps,L,k] int32) where
     predict[t,l] is the successor set of demand[t,l], i.e. the lookahead
     guess for layer l+1 (for l = L-1: layer 0 of step t+1)."""
     r = stream(seed, tag, L, E, k, steps)
-    perms = np.stack([stream(seed, tag, "perm", l, E).permutation(E) for l in range(L)])
+    ms = seed if model_seed is None else model_seed
+    perms = np.stack([stream(ms, tag, "perm", l, E).permutation(E) for l in range(L)])
     rank_of = np.empty_like(perms)
     for l in range(L):
         rank_of[l, perms[l]] = np.arange(E)

@@ -268,3 +268,55 @@ def test_host_cache_capacity_and_failed_copy():
             abi.moe_cache_stage(hc.h, 0, [1, 1], abi.STAGE_DEMAND)
     finally:
         hc.close()
+
+
+@pytest.mark.parametrize("cap,per_layer,n_pin", [(13, False, 5), (24, False, 30), (40, True, 6)])
+def test_host_cache_hot_store_equals_oracle_sim(orc, cap, per_layer, n_pin):
+    # usage learnt from a history trace (set through moe_cache_usage_set), a
+    # first pin before step 0 and a re-pin before step 12 from the counts so
+    # far; the event log, the counters and the usage counts equal the oracle's
+    L_, E, k, steps = 4, 32, 4, 25
+    hist, _ = synth.zipf_trace(12, L_, E, k, steps)
+    usage0 = np.bincount((np.arange(L_)[None, :, None] * E + hist).ravel(),
+                         minlength=L_ * E).astype(np.int64)
+    dem, pred = synth.zipf_trace(11, L_, E, k, steps)
+    pin = np.full(steps, -1, np.int32)
+    pin[0], pin[12] = n_pin, n_pin
+    hc = HostCache(L_, E, cap, per_layer)
+    try:
+        abi.moe_cache_usage_set(hc.h, usage0)
+        for t in range(steps):
+            if pin[t] >= 0:
+                abi.moe_cache_pin_hot(hc.h, int(pin[t]), k)
+            run_trace(hc, dem[t:t + 1], pred[t:t + 1])
+        log = abi.moe_cache_event_log(hc.h)
+        stats = abi.moe_cache_stats_get(hc.h)
+        usage = abi.moe_cache_usage_get(hc.h, L_ * E)
+    finally:
+        hc.close()
+    ev, st, u = orc.cache_sim_hot(L_, E, k, cap, dem, pred, wrap=False, per_layer=per_layer,
+                                  usage_init=usage0, pin_before=pin)
+    assert np.array_equal(log, ev)
+    for key in st:
+        assert stats[key] == st[key], key
+    assert np.array_equal(usage, u)
+    assert stats["pinned"] > 0
+
+
+def test_host_cache_pin_needs_no_locked_slot_and_valid_usage():
+    hc = HostCache(2, 16, 8)
+    try:
+        abi.moe_cache_stage(hc.h, 0, [1, 2], abi.STAGE_DEMAND)
+        with pytest.raises(abi.MoEError) as ei:
+            abi.moe_cache_pin_hot(hc.h, 2, 2)                 # layer 0 still holds slots
+        assert ei.value.status == abi.E_INVAL
+        abi.moe_cache_release(hc.h, 0)
+        abi.moe_cache_pin_hot(hc.h, 2, 2)
+        assert abi.moe_cache_stats_get(hc.h)["pinned"] == 2
+        bad = np.zeros(32, np.int64)
+        bad[3] = -1
+        with pytest.raises(abi.MoEError):
+            abi.moe_cache_usage_set(hc.h, bad)
+        assert abi.moe_cache_usage_get(hc.h, 32)[[1, 2]].tolist() == [1, 1]
+    finally:
+        hc.close()

@@ -165,3 +165,116 @@ def test_trace_lookahead_precision_near_page_figure():
             hit += len(set(pred[t, l].tolist()) & set(dem[nt, nl].tolist()))
             tot += k
     assert 0.66 < hit / tot < 0.80
+
+
+# ---------------------------------------------------------------------------
+# learned pinned hot-store
+# ---------------------------------------------------------------------------
+EV_PIN_FILL, EV_PIN_KEEP = 6, 7
+
+
+def textbook_lru_pinned(accesses, capacity, pinned):
+    """Demand-only LRU with a fixed set of pinned keys loaded first (in the
+    given order into the lowest free slots) that are never evicted.  Returns
+    the number of misses of `accesses` (the pin fills are not counted)."""
+    order, where = [], {}
+    free = list(range(capacity))
+    for key in pinned:
+        where[key] = free.pop(0)
+    misses = 0
+    for key in accesses:
+        if key in where:
+            if key in order:
+                order.remove(key)
+                order.append(key)
+            continue
+        misses += 1
+        if free:
+            slot = free.pop(0)
+        else:
+            victim = order.pop(0)
+            slot = where.pop(victim)
+        where[key] = slot
+        order.append(key)
+    return misses
+
+
+def test_usage_counts_every_demand_access(orc):
+    L, E, k, steps = 3, 20, 4, 40
+    dem, pred = _trace(5, L, E, k, steps)
+    _, st, usage = orc.cache_sim_hot(L, E, k, 30, dem, pred)
+    keys = (np.arange(L)[None, :, None] * E + dem).ravel()
+    assert np.array_equal(usage, np.bincount(keys, minlength=L * E))
+    assert usage.sum() == st["demand_hits"] + st["demand_misses"]
+
+
+def test_pinned_set_is_the_top_n_by_count(orc):
+    # one layer of 10 experts, k = 2; the first 7 steps make the counts
+    # 7:5, 3:4, 1:2, 9:2, 4:1 (1 and 9 tie: the lower key first), so pinning 3
+    # before step 7 pins 7, 3, 1.  With 5 more uses of expert 2 given up
+    # front, 2 ties 7 at 5 and comes first: 2 (copied in), 7, 3.
+    L, E, k = 1, 10, 2
+    rows = [[7, 3], [7, 3], [7, 1], [3, 9], [7, 9], [7, 3], [1, 4], [7, 1], [4, 5]]
+    dem = np.array(rows, np.int32).reshape(len(rows), 1, 2)
+    pin = np.full(len(rows), -1, np.int32)
+    pin[7] = 3
+    ev, st, usage = orc.cache_sim_hot(L, E, k, 8, dem, pin_before=pin)
+    pins = [(kind, e) for kind, l, e, s in ev.tolist() if kind in (EV_PIN_FILL, EV_PIN_KEEP)]
+    assert pins == [(EV_PIN_KEEP, 7), (EV_PIN_KEEP, 3), (EV_PIN_KEEP, 1)]
+    assert st["pinned"] == 3 and st["pin_fills"] == 0
+    init = np.zeros(E, np.int64)
+    init[2] = 5
+    ev, st, _ = orc.cache_sim_hot(L, E, k, 8, dem, pin_before=pin, usage_init=init)
+    pins = [(kind, e) for kind, l, e, s in ev.tolist() if kind in (EV_PIN_FILL, EV_PIN_KEEP)]
+    assert pins == [(EV_PIN_FILL, 2), (EV_PIN_KEEP, 7), (EV_PIN_KEEP, 3)]
+    assert st["pin_fills"] == 1
+
+
+def test_pinned_keys_are_never_evicted_and_reserve_holds(orc):
+    L, E, k, steps, cap = 2, 24, 4, 60, 12
+    dem, pred = _trace(9, L, E, k, steps)
+    pin = np.full(steps, -1, np.int32)
+    pin[20] = 100                        # more than fits: capacity - k = 8 pinned
+    ev, st, _ = orc.cache_sim_hot(L, E, k, cap, dem, pred, pin_before=pin)
+    assert st["pinned"] == cap - k
+    pinned, seen_pin = set(), False
+    for kind, l, e, s in ev.tolist():
+        if kind in (EV_PIN_FILL, EV_PIN_KEEP):
+            pinned.add((l, e))
+            seen_pin = True
+        elif kind == EV_EVICT and seen_pin:
+            assert (l, e) not in pinned
+    assert len(pinned) == cap - k
+    assert st["demand_hits"] + st["demand_misses"] == steps * L * k
+
+
+def test_capacity_above_keys_only_compulsory_misses_with_pins(orc):
+    L, E, k, steps = 2, 12, 3, 50
+    dem, pred = _trace(4, L, E, k, steps)
+    pin = np.full(steps, -1, np.int32)
+    pin[10] = 6
+    pin[30] = 9
+    _, st, _ = orc.cache_sim_hot(L, E, k, L * E, dem, pred, pin_before=pin)
+    assert st["demand_misses"] + st["prefetch_issued"] + st["pin_fills"] == \
+        len(np.unique((np.arange(L)[None, :, None] * E + dem).ravel()) if pred is None else
+            np.unique(np.concatenate([(np.arange(L)[None, :, None] * E + dem).ravel(),
+                                      ((np.arange(L)[None, :, None] + 1) % L * E + pred).ravel()])))
+    assert st["evictions"] == 0
+
+
+@pytest.mark.parametrize("cap,n_pin", [(8, 3), (10, 6), (16, 4)])
+def test_demand_only_with_pins_equals_textbook_pinned_lru(orc, cap, n_pin):
+    # Usage learnt over a first trace, pinned before the second: the misses of
+    # the second trace equal those of a list-based LRU whose pinned keys were
+    # loaded first and are never evicted.
+    L, E, k, steps = 1, 24, 2, 60
+    hist, _ = _trace(21, L, E, k, steps)
+    usage = np.bincount(hist.ravel(), minlength=E).astype(np.int64)
+    dem, _ = _trace(22, L, E, k, steps)
+    pin = np.full(steps, -1, np.int32)
+    pin[0] = n_pin
+    _, st, _ = orc.cache_sim_hot(L, E, k, cap, dem, usage_init=usage, pin_before=pin)
+    top = sorted(range(E), key=lambda e: (-usage[e], e))[:n_pin]
+    want = textbook_lru_pinned([int(e) for e in dem.ravel()], cap, top)
+    assert st["demand_misses"] == want
+    assert st["pin_fills"] == n_pin

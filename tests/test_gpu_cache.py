@@ -54,15 +54,18 @@ class Stack:
         abi.moe_host_free_pinned(self.host)
 
 
-def _run(stk, demand, predict, steps):
+def _run(stk, demand, predict, steps, pins=None):
     """The streaming loop: layer l runs through the cache (DEMAND inside the
     forward), then the guess for the next layer is prefetched and layer l is
-    released; every output is checked against the resident layer."""
+    released; every output is checked against the resident layer.  pins[t]
+    (when >= 0) pins that many hottest keys before step t."""
     used = np.empty_like(demand[:steps])
     idx = torch.empty((1, K), dtype=torch.int32, device="cuda")
     gw = torch.empty((1, K), dtype=torch.float32, device="cuda")
     out = torch.empty((1, H), dtype=torch.float32, device="cuda")
     for t in range(steps):
+        if pins is not None and pins[t] >= 0:
+            abi.moe_cache_pin_hot(stk.cache, int(pins[t]), K)
         for l in range(L_):
             b = synth.forcing_bias(E, demand[t, l])
             stk.bias.copy_(torch.from_numpy(b))
@@ -162,3 +165,36 @@ def test_layer_forward_rejects_layer_out_of_range_before_enqueue(layer):
         assert abi.moe_cache_stats_get(stk.cache)["bytes_copied"] == 0
     finally:
         stk.close()
+
+
+@pytest.mark.parametrize("n_slots,n_pin", [(9, 4), (14, 8)])
+def test_hot_store_pins_equal_oracle_and_keep_placement_invariance(n_slots, n_pin):
+    # usage from an earlier session of the same routing model, pins before
+    # step 0 and again before step 3; outputs stay bit-identical to the
+    # resident layers, and the event log, counters and usage equal the
+    # oracle's hot-store replay
+    steps = 6
+    hist, _ = synth.zipf_trace(17, L_, E, K, 12, model_seed=7)
+    usage0 = np.bincount((np.arange(L_)[None, :, None] * E + hist).ravel(),
+                         minlength=L_ * E).astype(np.int64)
+    demand, predict = synth.zipf_trace(7, L_, E, K, steps)
+    pins = np.full(steps, -1, np.int32)
+    pins[0], pins[3] = n_pin, n_pin
+    stk = Stack(n_slots)
+    try:
+        abi.moe_cache_usage_set(stk.cache, usage0)
+        used = _run(stk, demand, predict, steps, pins)
+        log = abi.moe_cache_event_log(stk.cache)
+        stats = abi.moe_cache_stats_get(stk.cache)
+        usage = abi.moe_cache_usage_get(stk.cache, L_ * E)
+    finally:
+        stk.close()
+    ev, st, u = oracle.cache_sim_hot(L_, E, K, n_slots, used, predict[:steps], wrap=True,
+                                     usage_init=usage0, pin_before=pins)
+    assert np.array_equal(log, ev)
+    for key in st:
+        assert stats[key] == st[key], key
+    assert np.array_equal(usage, u)
+    assert stats["pinned"] == min(n_pin, n_slots - K)
+    assert stats["bytes_copied"] == stk.blob * (stats["demand_misses"] + stats["prefetch_issued"] +
+                                                stats["pin_fills"])

@@ -605,3 +605,43 @@ def test_mx_layer_identical_experts(orc):
     for t in range(T):
         want = rs * _mx_expert_fp64(orc, xf[t], one)
         assert np.allclose(out0[t], want, rtol=1e-5, atol=1e-5 * np.abs(want).max())
+
+
+# ---------------------------------------------------------------------------
+# router lookahead and the residual composition of a stack
+# ---------------------------------------------------------------------------
+def test_residual_bf16_worked_values(orc):
+    # 1 + 2*0.25 = 1.5 exactly; 1 + 1*2^-8 is the midpoint between bf16 1 and
+    # 1 + 2^-7: ties to even -> 1; 1 + 3*2^-9 rounds up to 1 + 2^-7; the
+    # product gamma*y is rounded to fp32 before the add (gamma 1/3 * 3 gives
+    # 1.0000000298 in fp32, so 2 + that -> bf16 3)
+    x = synth.f32_to_bf16_bits(np.array([1.0, 1.0, 1.0, 2.0], np.float32))
+    y = np.array([0.25, 2 ** -8, 3 * 2 ** -9, 3.0], np.float32)
+    g = np.float32(1.0 / 3.0)
+    out = orc.residual_bf16(x[:3], y[:3], 1.0)
+    assert synth.bf16_bits_to_f32(out).tolist() == [1.25, 1.0, 1.0 + 2 ** -7]
+    out = orc.residual_bf16(x[:1], y[:1], 2.0)
+    assert synth.bf16_bits_to_f32(out).tolist() == [1.5]
+    out = orc.residual_bf16(x[3:], y[3:], g)
+    assert synth.bf16_bits_to_f32(out).tolist() == [3.0]
+
+
+def test_lookahead_is_the_next_router_on_the_current_state(orc):
+    # The prediction is the top-k of sigmoid(x_l . Wr_next) + b_next, checked
+    # by a brute-force ranking of exact rational logits; with gamma = 0 the
+    # next layer's input is x_l itself, so the prediction is the next layer's
+    # actual routing and precision is 1.
+    r = np.random.default_rng(31)
+    T, H, E, k = 3, 48, 12, 3
+    x = synth.f32_to_bf16_bits(r.standard_normal((T, H)).astype(np.float32))
+    W1 = (r.standard_normal((E, H)) * 0.2).astype(np.float32)
+    b1 = (r.standard_normal(E) * 0.05).astype(np.float32)
+    pred = orc.lookahead(x, W1, b1, k)
+    L = _exact_logits(x, W1)
+    for t in range(T):
+        c = [1.0 / (1.0 + math.exp(-L[t, e])) + float(b1[e]) for e in range(E)]
+        assert pred[t].tolist() == sorted(range(E), key=lambda e: (-c[e], e))[:k]
+    x1 = orc.residual_bf16(x, np.ones((T, H), np.float32), 0.0)
+    assert np.array_equal(x1, x)
+    actual, _ = orc.router(x1, W1, b1, k, 1.0)
+    assert np.array_equal(actual, pred)
