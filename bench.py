@@ -33,6 +33,9 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s (decode bs1, prefill 4096) + % HBM BW / % int8 MFMA peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, datasheet
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, datasheet
+# MI355X dense MFMA peaks, datasheet (TFLOP/s); an fp8 x fp4 MX MFMA runs at
+# the rate of its wider operand, fp8
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
 
 H, F, E, K_TOP, G = 6144, 2048, 256, 8, 32
 R_SCALE = 2.5
@@ -318,7 +321,9 @@ def run_prefill(args, lay):
 
 def run_mx(args):
     """MXFP4 wide layer: hidden 7168, 384 routed + 1 shared, F 2048, top-8,
-    64 tokens per call, routed scale 1.0, uniform routing bias."""
+    64 tokens per call, routed scale 1.0, uniform routing bias.  Timed on the
+    MX MFMA (the default kernel) and on the bf16 MFMA over exactly widened
+    weights."""
     import torch
     from quantized_expert_ffn_topk_amd import abi, synth
     from quantized_expert_ffn_topk_amd.layer import Layer, make_desc
@@ -336,59 +341,77 @@ def run_mx(args):
     idx, w, out = lay._outs(Tm)
     stream = torch.cuda.Stream()
     sh = abi.stream_handle(stream)
+    blob = abi.moe_blob_bytes(desc)
 
     def call(i):
         abi.moe_layer_forward(lay.ctx, xs[i % 4], Tm, lay.weights, None, 0, idx, w, out, sh)
 
-    for i in range(3):
-        call(i)
-    torch.cuda.synchronize()
-    n = args.mx_calls
-    uniq = []
-    t0 = time.perf_counter()
-    for i in range(n):
-        call(i)
-    stream.synchronize()
-    dt = (time.perf_counter() - t0) / n
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n)]
-    for i in range(n):
-        evs[i][0].record(stream)
-        call(i)
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    call_ms = percentiles([a.elapsed_time(b) for a, b in evs])
-    for i in range(4):                     # experts touched per input
-        call(i)
+    def measure(path):
+        lay.set_path(path)
+        for i in range(3):
+            call(i)
         torch.cuda.synchronize()
-        uniq.append(len(np.unique(idx.cpu().numpy())))
-    abi.moe_ctx_profile(lay.ctx, True)
-    abi.moe_ctx_profile_read(lay.ctx)
-    for i in range(n):
-        call(i)
-    torch.cuda.synchronize()
-    prof = abi.moe_ctx_profile_read(lay.ctx)
-    abi.moe_ctx_profile(lay.ctx, False)
-    kus = {k: 1e3 * v[0] / v[1] for k, v in prof.items() if v[1]}
-    blob = abi.moe_blob_bytes(desc)
-    touched = float(np.mean(uniq)) + 1.0
-    layer_bytes = touched * blob + Em * Hm * 4
-    ffn_us = kus.get("gateup", 0.0) + kus.get("down", 0.0)
+        n = args.mx_calls
+        uniq = []
+        t0 = time.perf_counter()
+        for i in range(n):
+            call(i)
+        stream.synchronize()
+        dt = (time.perf_counter() - t0) / n
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for i in range(n):
+            evs[i][0].record(stream)
+            call(i)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        call_ms = percentiles([a.elapsed_time(b) for a, b in evs])
+        for i in range(4):                     # experts touched per input
+            call(i)
+            torch.cuda.synchronize()
+            uniq.append(len(np.unique(idx.cpu().numpy())))
+        abi.moe_ctx_profile(lay.ctx, True)
+        abi.moe_ctx_profile_read(lay.ctx)
+        for i in range(n):
+            call(i)
+        torch.cuda.synchronize()
+        prof = abi.moe_ctx_profile_read(lay.ctx)
+        abi.moe_ctx_profile(lay.ctx, False)
+        kus = {k: 1e3 * v[0] / v[1] for k, v in prof.items() if v[1]}
+        touched = float(np.mean(uniq)) + 1.0
+        layer_bytes = touched * blob + Em * Hm * 4
+        ffn_us = kus.get("gateup", 0.0) + kus.get("down", 0.0)
+        # algorithmic MFMA work of the three projections over T*(k+1) rows
+        flops = 2.0 * Tm * (K_TOP + 1) * 3 * Hm * Fm
+        return {
+            "tokens_per_s": Tm / dt,
+            "ms_per_call": 1e3 * dt,
+            "ms_per_call_events": call_ms,
+            "experts_touched_per_call": touched,
+            "hbm": {"bytes_per_call": layer_bytes,
+                    "layer_GBs": layer_bytes / dt / 1e9,
+                    "layer_frac": layer_bytes / dt / 1e9 / HBM_PEAK_GBS,
+                    "expert_ffn_GBs": touched * blob / (ffn_us * 1e-6) / 1e9 if ffn_us else None},
+            "mfma": {"flops_per_call": flops,
+                     "TFLOPs": flops / (ffn_us * 1e-6) / 1e12 if ffn_us else None},
+            "kernels_us": {k: round(v, 2) for k, v in kus.items()},
+        }
+
+    res = measure(abi.PATH_AUTO)
+    if res["mfma"]["TFLOPs"] is not None:
+        res["mfma"]["peak_TFLOPs"] = MFMA_PEAK_TFLOPS["fp8"]
+        res["mfma"]["frac"] = res["mfma"]["TFLOPs"] / MFMA_PEAK_TFLOPS["fp8"]
+    bf = measure(abi.PATH_MX_BF16)
+    if bf["mfma"]["TFLOPs"] is not None:
+        bf["mfma"]["peak_TFLOPs"] = MFMA_PEAK_TFLOPS["bf16"]
+        bf["mfma"]["frac"] = bf["mfma"]["TFLOPs"] / MFMA_PEAK_TFLOPS["bf16"]
     lay.close()
-    return {
-        "workload": "MXFP4 wide layer: hidden 7168, 384 routed + 1 shared experts, FFN 2048, "
-                    "top-8, E2M1 + E8M0 per 32, bf16 activations, 64 tokens per call, routed "
-                    "scale 1.0, bias U(-0.01, 0.01)",
-        "tokens_per_s": Tm / dt,
-        "ms_per_call": 1e3 * dt,
-        "ms_per_call_events": call_ms,
-        "experts_touched_per_call": touched,
-        "hbm": {"bytes_per_call": layer_bytes,
-                "layer_GBs": layer_bytes / dt / 1e9,
-                "layer_frac": layer_bytes / dt / 1e9 / HBM_PEAK_GBS,
-                "expert_ffn_GBs": touched * blob / (ffn_us * 1e-6) / 1e9 if ffn_us else None},
-        "kernels_us": {k: round(v, 2) for k, v in kus.items()},
-    }
+    res["workload"] = ("MXFP4 wide layer: hidden 7168, 384 routed + 1 shared experts, FFN 2048, "
+                       "top-8, E2M1 + E8M0 per 32, bf16 activations, 64 tokens per call, routed "
+                       "scale 1.0, bias U(-0.01, 0.01)")
+    res["kernel"] = "MX MFMA (v_mfma_scale_f32_16x16x128_f8f6f4), activations split in two E4M3 parts"
+    res["bf16_mfma_path"] = dict(bf, kernel="bf16 MFMA on exactly widened weights")
+    return res
 
 
 def decode_gemv_roofline(kus, g):

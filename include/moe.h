@@ -48,6 +48,8 @@ typedef int32_t moe_status;
 #define MOE_PATH_AUTO  0       /* GEMV kernels for few tokens, MFMA otherwise */
 #define MOE_PATH_GEMV  1
 #define MOE_PATH_MFMA  2
+#define MOE_PATH_MX_BF16 3     /* MXFP4 layers: weights widened to exact bf16 on the bf16 MFMA
+                                  instead of the MX MFMA (exact products, plain fp32 sums) */
 
 /* Shape and numerics of one MoE layer.
  *  hidden H, ffn F: multiples of 256.  n_experts E in [1, 1024].
@@ -91,7 +93,12 @@ typedef struct moe_cache moe_cache;
 moe_status moe_ctx_create(int32_t device, const moe_layer_desc *desc,
                           int32_t max_tokens, moe_ctx **out);
 void moe_ctx_destroy(moe_ctx *ctx);
-/* Kernel path for the expert FFNs (MOE_PATH_*).  Results do not depend on it. */
+/* Kernel path for the expert FFNs (MOE_PATH_*).  For int4 layers results do
+ * not depend on it (every path gives the same bits).  MXFP4 layers run on the
+ * gfx950 MX MFMA by default (activations split into two E4M3 parts; its
+ * internal sums measured to ~3e-4 of the largest output on the test layers)
+ * or, with MOE_PATH_MX_BF16, on the bf16 MFMA with exact bf16 weights (~1e-7);
+ * both within the 2e-3 output bar. */
 moe_status moe_ctx_set_path(moe_ctx *ctx, int32_t path);
 
 /* ---- weight packing (host only, no GPU needed) -----------------------------

@@ -16,7 +16,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
 OK, E_INVAL, E_UNSUPPORTED, E_NOMEM, E_HIP, E_CAPACITY = range(6)
 WFMT_INT4, WFMT_MXFP4 = 0, 1
 DT_F32, DT_BF16 = 0, 1
-PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
+PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_MX_BF16 = 0, 1, 2, 3
 CACHE_GLOBAL_LRU, CACHE_PER_LAYER_LRU = 0, 1
 CACHE_BACKEND_HIP, CACHE_BACKEND_HOST = 0, 1
 STAGE_DEMAND, STAGE_PREFETCH = 0, 1

@@ -179,10 +179,13 @@ extern "C" moe_status moe_ctx_set_path(moe_ctx *ctx, int32_t path)
 {
     if (!ctx)
         return fail(MOE_E_INVAL, "ctx is NULL");
-    if (path != MOE_PATH_AUTO && path != MOE_PATH_GEMV && path != MOE_PATH_MFMA)
+    if (path != MOE_PATH_AUTO && path != MOE_PATH_GEMV && path != MOE_PATH_MFMA &&
+        path != MOE_PATH_MX_BF16)
         return fail(MOE_E_INVAL, "unknown path %d", path);
     if (path == MOE_PATH_MFMA && ctx->d.wfmt != MOE_WFMT_INT4)
-        return fail(MOE_E_UNSUPPORTED, "the MFMA path covers int4 weights");
+        return fail(MOE_E_UNSUPPORTED, "the int8 MFMA path covers int4 weights");
+    if (path == MOE_PATH_MX_BF16 && ctx->d.wfmt != MOE_WFMT_MXFP4)
+        return fail(MOE_E_UNSUPPORTED, "the bf16 MX path covers MXFP4 weights");
     ctx->path = path;
     return MOE_OK;
 }

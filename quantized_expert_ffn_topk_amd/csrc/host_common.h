@@ -37,8 +37,10 @@ struct moe_ctx {
     // MFMA path: tile work list
     int32_t *tiles = nullptr, *n_tiles = nullptr;
     int max_tiles = 0;
-    // MXFP4 path: bf16 activations of h
+    // MXFP4 path: bf16 activations of h; activation rows split into E4M3
+    // hi/lo parts [rows][K] and their E8M0 scales [rows][K/32]
     uint16_t *hb = nullptr;
+    uint8_t *mx_hi = nullptr, *mx_lo = nullptr, *mx_ehi = nullptr, *mx_elo = nullptr;
     // small device constants for single-blob projections
     int32_t *zero1 = nullptr, *one1 = nullptr, *dbg_cnt = nullptr, *ident = nullptr;
     int last_T = 0;
@@ -100,8 +102,15 @@ moe_status ws_plan(moe_ctx *c, Fn &&f)
     WS(cs, 2 * E, WS_DATA);
     WS(tiles, (size_t)c->max_tiles * 2, WS_DATA);
     WS(n_tiles, 4, WS_DATA);
-    if (d.wfmt == MOE_WFMT_MXFP4)
+    if (d.wfmt == MOE_WFMT_MXFP4) {
+        // split buffers sized for the larger of the two uses (tokens x H, slots x F)
+        const size_t split = (T * H > T * S * F) ? T * H : T * S * F;
         WS(hb, T * S * F, WS_DATA);
+        WS(mx_hi, split, WS_DATA);
+        WS(mx_lo, split, WS_DATA);
+        WS(mx_ehi, split / 32, WS_DATA);
+        WS(mx_elo, split / 32, WS_DATA);
+    }
     WS(ident, T, WS_DEBUG);
     WS(zero1, 1, WS_DEBUG);
     WS(one1, 1, WS_DEBUG);

@@ -71,3 +71,21 @@ def test_bf16_check_accepts_rounding_and_catches_a_wrong_step():
     mid = np.array([1.0 + 2 ** -8, 2.0], np.float32)
     up = synth.f32_to_bf16_bits(np.array([1.0 + 2 ** -7, 2.0], np.float32))
     check_bf16_out(up, mid)
+
+
+def test_bf16_check_without_same_rounding_keeps_the_bar():
+    from quantized_expert_ffn_topk_amd import synth
+    from tests.gpu_common import check_bf16_out
+    r = np.random.default_rng(1).standard_normal(1000).astype(np.float32)
+    # sums off by 1e-4 of the largest output round to other bf16 values: fine
+    # without same_rounding, caught with it
+    near = r + np.float32(1e-4) * np.abs(r).max()
+    bits = synth.f32_to_bf16_bits(near)
+    with pytest.raises(AssertionError):
+        check_bf16_out(bits, r)
+    e, _ = check_bf16_out(bits, r, same_rounding=False)
+    assert e <= 1.1e-4
+    # 3e-3 of the largest output away: outside the bar either way
+    far = synth.f32_to_bf16_bits(r + np.float32(3e-3) * np.abs(r).max())
+    with pytest.raises(AssertionError):
+        check_bf16_out(far, r, same_rounding=False)

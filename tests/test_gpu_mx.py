@@ -1,7 +1,9 @@
 """GPU parity of the MXFP4 expert path (E2M1 weights with E8M0 scales per 32,
 bf16 activations) through the C ABI against the oracle: routing, the bf16
 SwiGLU rows, the layer outputs, given routing, and the wide MXFP4 layer at full
-size on sampled outputs."""
+size on sampled outputs.  Both kernels are checked: the MX MFMA (default;
+activations split into two E4M3 parts, the MFMA's own internal sums) and the
+bf16 MFMA on exactly widened weights (MOE_PATH_MX_BF16)."""
 import numpy as np
 import pytest
 
@@ -27,11 +29,11 @@ class MxCase:
         self.b = synth.uniform_bias(seed, E)
         self.x = synth.activations(seed, T, H) if x is None else x
 
-    def layer(self, max_tokens=None, out_dtype=abi.DT_F32):
+    def layer(self, max_tokens=None, out_dtype=abi.DT_F32, path=abi.PATH_AUTO):
         desc = make_desc(self.H, self.F, self.E, self.k, self.n_shared, 32, self.r,
                          abi.WFMT_MXFP4, out_dtype)
         return Layer(desc, self.Wr, self.b, self.distinct, self.shared, self.emap,
-                     max_tokens=max_tokens or self.T)
+                     max_tokens=max_tokens or self.T, path=path)
 
     def oracle_layer(self, out_rows=None):
         return oracle.mx_layer(self.x, self.Wr, self.b, self.distinct, self.shared, self.k,
@@ -46,25 +48,30 @@ def _check_mx_out(got, want):
     return e
 
 
+PATHS = [pytest.param(abi.PATH_AUTO, id="mxmfma"), pytest.param(abi.PATH_MX_BF16, id="bf16mfma")]
+
+
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("T,shared", [(1, 1), (5, 0), (23, 1)])
-def test_mx_layer_matches_oracle(T, shared):
+def test_mx_layer_matches_oracle(T, shared, path):
     c = MxCase(31, T, 512, 256, 16, 4, shared, r=1.5)
-    lay = c.layer()
+    lay = c.layer(path=path)
     idx, w, out = lay.forward(lay.x_tensor(c.x))
     torch.cuda.synchronize()
     idx_o, w_o, out_o = c.oracle_layer()
     _, _, _, _, ch = oracle.router(c.x, c.Wr, c.b, c.k, c.r, want=True)
     check_routing(idx.cpu().numpy(), w.cpu().numpy(), idx_o, w_o, ch)
     e = _check_mx_out(out.cpu().numpy(), out_o)
-    print("mx layer T=%d: max rel err %.3g" % (T, e))
+    print("mx layer T=%d path %d: max rel err %.3g" % (T, path, e))
     lay.close()
 
 
-def test_mx_swiglu_rows_match_oracle():
-    # bf16 h rows: equal to the oracle's except where the fp32 projection sits
-    # at a bf16 rounding boundary (then one bf16 ulp apart)
+def test_mx_swiglu_rows_match_oracle_bf16_path():
+    # exact bf16 products, fp32 sums: the bf16 h rows equal the oracle's except
+    # where the fp32 projection sits at a bf16 rounding boundary (then one bf16
+    # ulp apart)
     c = MxCase(32, 6, 1024, 512, 8, 2, 1)
-    lay = c.layer()
+    lay = c.layer(path=abi.PATH_MX_BF16)
     idx, _, _ = lay.forward(lay.x_tensor(c.x))
     torch.cuda.synchronize()
     S = c.k + 1
@@ -83,9 +90,33 @@ def test_mx_swiglu_rows_match_oracle():
     lay.close()
 
 
-def test_mx_expert_ffn_given_routing_and_determinism():
-    c = MxCase(33, 4, 512, 256, 12, 3, 1, r=2.0)
+def test_mx_swiglu_rows_mx_mfma():
+    # MX MFMA: each h row within the output bar of the oracle's row (distance
+    # to the row's largest |h|), the bf16 rounding of both sides included
+    c = MxCase(32, 6, 1024, 512, 8, 2, 1)
     lay = c.layer()
+    idx, _, _ = lay.forward(lay.x_tensor(c.x))
+    torch.cuda.synchronize()
+    S = c.k + 1
+    hb = lay.debug_read(7, (c.T, S, c.F), torch.int16).cpu().numpy().view(np.uint16)
+    ig = idx.cpu().numpy()
+    xf = synth.bf16_bits_to_f32(c.x)
+    worst = 0.0
+    for t in range(c.T):
+        for i in range(S):
+            ex = c.shared if i == c.k else c.distinct[c.emap[ig[t, i]]]
+            want = synth.bf16_bits_to_f32(oracle.mx_expert(xf[t], ex)["h_bf16"]).astype(np.float64)
+            got = synth.bf16_bits_to_f32(hb[t, i]).astype(np.float64)
+            worst = max(worst, float(np.abs(got - want).max() / np.abs(want).max()))
+    assert worst <= MAX_REL_ERR, worst
+    print("mx-mfma SwiGLU rows: max distance / row max %.3g" % worst)
+    lay.close()
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_mx_expert_ffn_given_routing_and_determinism(path):
+    c = MxCase(33, 4, 512, 256, 12, 3, 1, r=2.0)
+    lay = c.layer(path=path)
     xd = lay.x_tensor(c.x)
     idx, w, out1 = lay.forward(xd)
     out2 = lay.ffn(xd, idx, w)
@@ -94,14 +125,17 @@ def test_mx_expert_ffn_given_routing_and_determinism():
     lay.close()
 
 
-def test_mx_bf16_output():
+@pytest.mark.parametrize("path", PATHS)
+def test_mx_bf16_output(path):
     c = MxCase(34, 3, 512, 256, 8, 2, 1)
-    lay = c.layer(out_dtype=abi.DT_BF16)
+    lay = c.layer(out_dtype=abi.DT_BF16, path=path)
     _, _, out = lay.forward(lay.x_tensor(c.x))
     torch.cuda.synchronize()
     _, _, out_o = c.oracle_layer()
     got = out.view(torch.int16).cpu().numpy().view(np.uint16)
-    e, same = check_bf16_out(got, out_o)
+    # the MX MFMA's sums differ from fp32 ones by more than a few fp32 ulps,
+    # so only the 2e-3 bar beyond the bf16 rounding applies there
+    e, same = check_bf16_out(got, out_o, same_rounding=(path == abi.PATH_MX_BF16))
     print("mx bf16 output: max rel err %.3g, equal to the oracle's rounding %.5f" % (e, same))
     lay.close()
 
@@ -111,18 +145,25 @@ def test_mx_wide_layer_full_size():
     # tokens, uniform routing bias.  Routing checked for every token; the
     # outputs of all 64 tokens on 256 sampled columns against the fp64 oracle
     # (11 distinct weight sets behind a seeded random map of the 384 experts).
+    # Both kernels run on the same layer.
     H, F, E, k, T = 7168, 2048, 384, 8, 64
     c = MxCase(0, T, H, F, E, k, 1, r=1.0, n_distinct=11)
     lay = c.layer()
-    idx, w, out = lay.forward(lay.x_tensor(c.x))
-    torch.cuda.synchronize()
+    xd = lay.x_tensor(c.x)
+    outs = {}
+    for path in (abi.PATH_AUTO, abi.PATH_MX_BF16):
+        lay.set_path(path)
+        idx, w, out = lay.forward(xd)
+        torch.cuda.synchronize()
+        outs[path] = (idx.cpu().numpy(), w.cpu().numpy(), out.cpu().numpy())
+    lay.close()
     idx_o, w_o, lg, sc, ch = oracle.router(c.x, c.Wr, c.b, k, c.r, want=True)
-    check_routing(idx.cpu().numpy(), w.cpu().numpy(), idx_o, w_o, ch)
     rng = np.random.default_rng(2)
     cols = np.sort(rng.choice(H, 256, replace=False)).astype(np.int32)
     _, _, out_o = oracle_rows_parallel(
         lambda xs: oracle.mx_layer(xs, c.Wr, c.b, c.distinct, c.shared, k, c.r, out_rows=cols,
                                    expert_map=c.emap), c.x, np.arange(T))
-    e = _check_mx_out(out.cpu().numpy()[:, cols], out_o)
-    print("mx wide layer: max rel err %.3g over 64 tokens x 256 columns" % e)
-    lay.close()
+    for path, (idx, w, out) in outs.items():
+        check_routing(idx, w, idx_o, w_o, ch)
+        e = _check_mx_out(out[:, cols], out_o)
+        print("mx wide layer path %d: max rel err %.3g over 64 tokens x 256 columns" % (path, e))
