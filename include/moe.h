@@ -17,8 +17,14 @@
  *  - Every call validates its arguments before enqueuing anything and returns
  *    a status; nothing aborts or throws across the ABI.  moe_last_error()
  *    gives the message of the last non-OK status of the calling thread.
- *  - Outputs are bitwise identical for identical inputs, whatever the grid,
- *    the kernel path (GEMV or MFMA), the cache state or the stream timing.
+ *  - Outputs are bitwise identical for identical inputs and the same kernel
+ *    path, whatever the grid, the cache state or the stream timing (every sum
+ *    has a fixed order).  Across the int4 paths (one-token, GEMV, MFMA) the
+ *    expert projections and the combine give the same bits too (their sums
+ *    are exact); the router's fp64 logits are summed in an order of each
+ *    router kernel, so two paths may differ in the logits' last bits and,
+ *    where two biased scores lie that close, in the routing.  The two MXFP4
+ *    kernels differ in their sums (moe_ctx_set_path).
  *  - A moe_ctx is used by one host thread at a time.
  */
 #ifndef MOE_H
