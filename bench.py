@@ -143,9 +143,10 @@ def run_decode(args, lay):
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        ev0.record(stream)
-        g.replay()
-        ev1.record(stream)
+        with torch.cuda.stream(stream):      # replay() launches on the current stream
+            ev0.record(stream)
+            g.replay()
+            ev1.record(stream)
         stream.synchronize()
         torch.cuda.synchronize()
         res["graph_s"] = time.perf_counter() - t0

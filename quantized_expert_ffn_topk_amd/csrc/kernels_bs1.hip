@@ -538,14 +538,112 @@ __device__ __forceinline__ double dnh_dot(const uint4 (&wv)[8], const uint16_t (
     return p;
 }
 
+// The shared expert's part of the block for SQ: wave q (0-3) of the four
+// after the k routed waves takes inputs [512q, 512q+512) of every half tile
+// (loads j = 2q, 2q+1 of the 8), codes only that quarter of the SwiGLU row
+// (amax still over the whole row) and leaves the quarter's exact sums in sP;
+// the four are added in the combine (exact, so the order does not matter).
 template <int NH>
-__global__ __launch_bounds__(64 * 9) void down_bs1h_kernel(Bs1Args a)
+__device__ __forceinline__ void down_shared_quarter(const Bs1Args &a, const uint8_t *blob, int q,
+                                                    int pr, int lane, const float4 (&hv)[8],
+                                                    int8_t *lq, double (*sP)[8 * NH],
+                                                    float *s_sc)
+{
+    const int r = lane & 7, c8 = lane >> 3, gs = a.group_shift, ai = a.k;
+    const int F = 2048;
+    uint4 wv[NH][2];
+    uint16_t sv[NH][2];
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+        const int hidx = NH * pr + i, t = hidx >> 1, hf = hidx & 1;
+        const uint4 *wp = reinterpret_cast<const uint4 *>(blob + a.dn_w + (size_t)t * a.dn_tile_w) +
+                          8 * hf + r + 16 * c8;
+        const uint16_t *sp = reinterpret_cast<const uint16_t *>(blob + a.dn_s + (size_t)t * a.dn_tile_s) +
+                             ((c8 >> gs) << 4) + 8 * hf + r;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * q + jj;
+            wv[i][jj] = load_stream16(wp + 128 * j);
+            sv[i][jj] = gload2(sp + (size_t)(128 >> gs) * j);
+        }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(hv[i].x), fabsf(hv[i].y)),
+                                 fmaxf(fabsf(hv[i].z), fabsf(hv[i].w))));
+    amax = wave_max(amax);
+    float inv = 0.0f, sc = 0.0f;
+    if (amax > 0.0f) {
+        inv = 127.0f / amax;
+        sc = amax / 127.0f;
+    }
+    // float4 i of the lane holds inputs 256 i + 4 lane ...: the quarter is i = 2q, 2q+1
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if ((i >> 1) != q)
+            continue;
+        const float vv[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w};
+        uint32_t packed = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float qv = fminf(fmaxf(rintf(vv[j] * inv), -127.0f), 127.0f);
+            packed |= ((uint32_t)(int)qv & 0xffu) << (8 * j);
+        }
+        const int o = 4 * (lane + 64 * i);
+        *reinterpret_cast<uint32_t *>(lq + o) = packed;
+        if (pr == 0)
+            *reinterpret_cast<uint32_t *>(a.qh + (size_t)ai * F + o) = packed;
+    }
+    if (lane == 0 && q == 0) {
+        *s_sc = sc;
+        if (pr == 0)
+            a.sh[ai] = sc;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0): this wave's codes
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+        double p = 0.0;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int c = 8 * (2 * q + jj) + c8;
+            const int4 *qa = reinterpret_cast<const int4 *>(lq + c * 32);
+            const int4 a0 = qa[0], a1 = qa[1];
+            const uint32_t wd[4] = {wv[i][jj].x, wv[i][jj].y, wv[i][jj].z, wv[i][jj].w};
+            int acc = 0;
+            acc = sdot4((int)((wd[0] << 4) & 0xf0f0f0f0u), a0.x, acc);
+            acc = sdot4((int)((wd[1] << 4) & 0xf0f0f0f0u), a0.y, acc);
+            acc = sdot4((int)((wd[2] << 4) & 0xf0f0f0f0u), a0.z, acc);
+            acc = sdot4((int)((wd[3] << 4) & 0xf0f0f0f0u), a0.w, acc);
+            acc = sdot4((int)(wd[0] & 0xf0f0f0f0u), a1.x, acc);
+            acc = sdot4((int)(wd[1] & 0xf0f0f0f0u), a1.y, acc);
+            acc = sdot4((int)(wd[2] & 0xf0f0f0f0u), a1.z, acc);
+            acc = sdot4((int)(wd[3] & 0xf0f0f0f0u), a1.w, acc);
+            p = fma((double)acc, (double)f16_to_f32(sv[i][jj]) * 0.0625, p);
+        }
+        p += xor_lane_d<8>(p);
+        p += xor_lane_d<16>(p);
+        p += xor_lane_d<32>(p);
+        if (lane < 8)
+            sP[q][8 * i + r] = p;
+    }
+}
+
+// SQ: k routed waves, then the shared expert over four K-quarter waves (k + 4
+// waves: for k = 8 every SIMD holds two routed waves and one quarter wave,
+// where one wave per slot puts three full waves on one SIMD).
+template <int NH, bool SQ>
+__global__ __launch_bounds__(64 * 12) void down_bs1h_kernel(Bs1Args a)
 {
     extern __shared__ __align__(16) unsigned char smem[];   // S rows of F codes
     __shared__ float sY[9][8 * NH];
+    __shared__ double sP[SQ ? 4 : 1][8 * NH];
+    __shared__ float s_sc;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 7, c8 = lane >> 3;
-    const int ai = wave, pr = blockIdx.x;
+    const bool shq = SQ && wave >= a.k;
+    const int ai = shq ? a.k : wave, pr = blockIdx.x;
     const int F = 2048;
     int8_t *lq = reinterpret_cast<int8_t *>(smem) + (size_t)ai * F;
 
@@ -563,7 +661,9 @@ __global__ __launch_bounds__(64 * 9) void down_bs1h_kernel(Bs1Args a)
     for (int i = 0; i < 8; ++i)
         hv[i] = hr[lane + 64 * i];
     const uint8_t *blob = bs1_slot_blob(a, ai);
-    if (blob) {
+    if (shq)
+        down_shared_quarter<NH>(a, blob, wave - a.k, pr, lane, hv, lq, sP, &s_sc);
+    else if (blob) {
         uint4 wa[8], wb[8];
         uint16_t sa[8], sb[8];
         dnh_load<NH>(blob, a, NH * pr, r, c8, wa, sa);
@@ -627,7 +727,18 @@ __global__ __launch_bounds__(64 * 9) void down_bs1h_kernel(Bs1Args a)
     }
     __syncthreads();
     if (threadIdx.x < 8 * NH) {
-        double o = a.n_shared ? (double)sY[a.k][threadIdx.x] : 0.0;
+        double o = 0.0;
+        if (SQ) {
+            // the quarter sums are exact, so is their sum: the shared row's y
+            // is that of one wave over the whole row
+            const double p = ((sP[0][threadIdx.x] + sP[1][threadIdx.x]) + sP[2][threadIdx.x]) +
+                             sP[3][threadIdx.x];
+            const float y = (float)(p * (double)s_sc);
+            a.Y[(size_t)a.k * a.H + 8 * NH * pr + threadIdx.x] = y;
+            o = (double)y;
+        } else if (a.n_shared) {
+            o = (double)sY[a.k][threadIdx.x];
+        }
         for (int i = 0; i < a.k; ++i) {
             const int ex = s_e[i];
             if (ex >= 0 && ex < a.ex.E)
@@ -737,10 +848,21 @@ hipError_t launch_down_bs1(const Bs1Args &a, hipStream_t st)
         if (nh > 3)
             nh = (nh % 2 == 0) ? 2 : 1;
         const dim3 g(a.H / (8 * nh));
+        // the shared expert over four K-quarter waves when it exists and the
+        // block stays within 12 waves
+        if (a.n_shared && a.k <= 8) {
+            const int nt = 64 * (a.k + 4);
+            switch (nh) {
+            case 1: launch(down_bs1h_kernel<1, true>, g, nt, lds, st, a); return hipGetLastError();
+            case 2: launch(down_bs1h_kernel<2, true>, g, nt, lds, st, a); return hipGetLastError();
+            case 3: launch(down_bs1h_kernel<3, true>, g, nt, lds, st, a); return hipGetLastError();
+            default: break;
+            }
+        }
         switch (nh) {
-        case 1: launch(down_bs1h_kernel<1>, g, 64 * S, lds, st, a); return hipGetLastError();
-        case 2: launch(down_bs1h_kernel<2>, g, 64 * S, lds, st, a); return hipGetLastError();
-        case 3: launch(down_bs1h_kernel<3>, g, 64 * S, lds, st, a); return hipGetLastError();
+        case 1: launch(down_bs1h_kernel<1, false>, g, 64 * S, lds, st, a); return hipGetLastError();
+        case 2: launch(down_bs1h_kernel<2, false>, g, 64 * S, lds, st, a); return hipGetLastError();
+        case 3: launch(down_bs1h_kernel<3, false>, g, 64 * S, lds, st, a); return hipGetLastError();
         default: break;
         }
     }
