@@ -202,7 +202,22 @@ def run_small_batches(args, lay):
             call(i)
         stream.synchronize()
         dt = (time.perf_counter() - t0) / n
-        res[str(T)] = {"tokens_per_s": T / dt, "us_per_step": 1e6 * dt}
+        # the same steps again with every launch stamped (library event ring)
+        abi.moe_ctx_profile(ctx, True)
+        abi.moe_ctx_profile_read(ctx)
+        for i in range(n):
+            call(i)
+        torch.cuda.synchronize()
+        prof = abi.moe_ctx_profile_read(ctx)
+        abi.moe_ctx_profile(ctx, False)
+        kus = {k: round(1e3 * v[0] / v[1], 2) for k, v in prof.items() if v[1]}
+        # distinct experts of a step (routed + shared) and their weight bytes
+        uniq = len(np.unique(idx.cpu().numpy())) + 1
+        blob = abi.moe_blob_bytes(lay.desc)
+        proj_us = kus.get("gateup", 0.0) + kus.get("down", 0.0)
+        res[str(T)] = {"tokens_per_s": T / dt, "us_per_step": 1e6 * dt, "kernels_us": kus,
+                       "experts_touched": uniq,
+                       "projections_GBs": uniq * blob / (proj_us * 1e-6) / 1e9 if proj_us else None}
     abi.moe_ctx_destroy(ctx)
     return res
 
