@@ -559,11 +559,11 @@ def run_stream(args, lay, W):
 
         warm = min(8, steps // 4)
 
-        def stream_pass(n_pin):
+        def stream_pass(n_pin, mode=abi.STAGE_PREFETCH):
             """The trace through a fresh cache; n_pin > 0: the hot-store, its
             usage loaded from the earlier session and the n_pin hottest keys
             pinned before the first step, re-pinned from the counts so far
-            every 32 steps."""
+            every 32 steps; mode None: demand staging only."""
             cache = abi.moe_cache_create(abi.moe_cache_desc(
                 0, L, E, blob, cap, C.addressof(ptrs), abi.CACHE_GLOBAL_LRU,
                 abi.CACHE_BACKEND_HIP))
@@ -576,8 +576,8 @@ def run_stream(args, lay, W):
                                             lay.shared_blob.data_ptr())
                 abi.moe_layer_forward(ctx, xs[t * L + l:t * L + l + 1], 1, wts, cache, l, idx, w,
                                       out, sh)
-                if l + 1 < L:
-                    abi.moe_cache_stage(cache, l + 1, predict[t, l], abi.STAGE_PREFETCH, sh)
+                if l + 1 < L and mode is not None:
+                    abi.moe_cache_stage(cache, l + 1, predict[t, l], mode, sh)
                 abi.moe_cache_release(cache, l, sh)
 
             for t in range(warm):
@@ -599,6 +599,8 @@ def run_stream(args, lay, W):
 
         dt, st = stream_pass(0)
         dt_hot, st_hot = stream_pass(args.stream_pins)
+        dt_dm, st_dm = stream_pass(0, None)
+        dt_id, st_id = stream_pass(0, abi.STAGE_PREFETCH_IDLE)
 
         # the same layer calls with every expert resident (the layer's own 256
         # device blobs, no cache) and the same host synchronisation on the
@@ -682,6 +684,25 @@ def run_stream(args, lay, W):
                                   if st_hot["copy_busy_ms"] > 0 else None),
             "stats": st_hot,
         },
+        "demand_only": {
+            "note": "the same trace and pool with the prefetch calls left out",
+            "tokens_per_s": n / dt_dm,
+            "demand_hit_rate": st_dm["demand_hits"] / (st_dm["demand_hits"] +
+                                                       st_dm["demand_misses"]),
+            "misses_per_token": st_dm["demand_misses"] / n,
+            "copies_per_token": st_dm["demand_misses"] / n,
+            "stats": st_dm,
+        },
+        "idle_prefetch": {
+            "note": "the same trace and pool, the guess prefetched only while the copy engine "
+                    "is idle (MOE_STAGE_PREFETCH_IDLE)",
+            "tokens_per_s": n / dt_id,
+            "demand_hit_rate": st_id["demand_hits"] / (st_id["demand_hits"] +
+                                                       st_id["demand_misses"]),
+            "misses_per_token": st_id["demand_misses"] / n,
+            "copies_per_token": (st_id["demand_misses"] + st_id["prefetch_issued"]) / n,
+            "stats": st_id,
+        },
     }
 
 
@@ -713,22 +734,21 @@ def run_stream_lookahead(args, lay):
         return abi.moe_layer_weights(Wr[l].data_ptr(), bias[l].data_ptr(), ptrs,
                                      lay.shared_blob.data_ptr())
 
-    def step(t, gamma, cache):
+    def step(t, gamma, cache, mode=abi.STAGE_PREFETCH):
         """One token through the 16 layers; returns per layer (actual ids,
         predicted ids for that layer or None)."""
         x = x0[t:t + 1]
         rec = []
         with torch.cuda.stream(stream):
             for l in range(L):
-                if l + 1 < L:
+                if l + 1 < L and (mode is not None or cache is None):
                     abi.moe_router_topk(ctx, x, 1, wts(l + 1, None), pred, pw, sh)
                     pred_host[l].copy_(pred[0], non_blocking=True)
                 abi.moe_layer_forward(ctx, x, 1, wts(l, None if cache else lay.ptrs.data_ptr()),
                                       cache, l, idx, w, out, sh)
                 if cache is not None:
-                    if l + 1 < L:      # the router sync above made the guess visible
-                        abi.moe_cache_stage(cache, l + 1, pred_host[l].numpy(),
-                                            abi.STAGE_PREFETCH, sh)
+                    if l + 1 < L and mode is not None:   # the router sync above made the guess visible
+                        abi.moe_cache_stage(cache, l + 1, pred_host[l].numpy(), mode, sh)
                     abi.moe_cache_release(cache, l, sh)
                 else:
                     stream.synchronize()
@@ -758,27 +778,62 @@ def run_stream_lookahead(args, lay):
             base[i * blob:(i + 1) * blob] = lay.blobs[i % len(lay.blobs)].cpu().numpy()
         ptrs = (C.c_void_p * (L * E))(*[host + ((l * E + e) % n_phys) * blob
                                          for l in range(L) for e in range(E)])
-        cache = abi.moe_cache_create(abi.moe_cache_desc(0, L, E, blob, 24 << 30, C.addressof(ptrs),
-                                                        abi.CACHE_GLOBAL_LRU, abi.CACHE_BACKEND_HIP))
-        warm = min(8, steps // 4)
-        for t in range(warm):
-            step(t, gamma, cache)
-        abi.moe_cache_reset_stats(cache)
-        hit = tot = 0
-        t0 = time.perf_counter()
-        for t in range(warm, steps):
-            act, pr = step(t, gamma, cache)
-            hit += sum(len(set(act[l + 1].tolist()) & set(pr[l].tolist())) for l in range(L - 1))
-            tot += (L - 1) * K_TOP
-        dt = time.perf_counter() - t0
-        st = abi.moe_cache_stats_get(cache)
-        abi.moe_cache_destroy(cache)
+        def session(cap, mode):
+            cache = abi.moe_cache_create(abi.moe_cache_desc(0, L, E, blob, cap, C.addressof(ptrs),
+                                                            abi.CACHE_GLOBAL_LRU, abi.CACHE_BACKEND_HIP))
+            try:
+                warm = min(8, steps // 4)
+                for t in range(warm):
+                    step(t, gamma, cache, mode)
+                abi.moe_cache_reset_stats(cache)
+                hit = tot = 0
+                t0 = time.perf_counter()
+                for t in range(warm, steps):
+                    act, pr = step(t, gamma, cache, mode)
+                    hit += sum(len(set(act[l + 1].tolist()) & set(pr[l].tolist()))
+                               for l in range(L - 1))
+                    tot += (L - 1) * K_TOP
+                dt = time.perf_counter() - t0
+                st = abi.moe_cache_stats_get(cache)
+            finally:
+                abi.moe_cache_destroy(cache)
+            n = steps - warm
+            dem = st["demand_hits"] + st["demand_misses"]
+            return {
+                "tokens_per_s": n / dt,
+                "ms_per_token": 1e3 * dt / n,
+                "demand_hit_rate": st["demand_hits"] / dem if dem else None,
+                "prefetch_precision": (st["prefetch_used"] / st["prefetch_issued"]
+                                       if st["prefetch_issued"] else None),
+                "prefetch_coverage": (st["prefetch_used"] / (st["prefetch_used"] + st["demand_misses"])
+                                      if st["prefetch_used"] + st["demand_misses"] else None),
+                "h2d_GBs_copy_busy": (st["bytes_copied"] / (st["copy_busy_ms"] * 1e-3) / 1e9
+                                      if st["copy_busy_ms"] > 0 else None),
+                "copies_per_token": (st["demand_misses"] + st["prefetch_issued"]) / n,
+                "misses_per_token": st["demand_misses"] / n,
+                "stats": st,
+            }, hit / tot
+
+        big, prec = session(24 << 30, abi.STAGE_PREFETCH)
+        # smaller pools: the same session with the guess prefetched, prefetched
+        # only into idle copy-engine time, and with demand staging only (no
+        # lookahead router either)
+        keys = ("tokens_per_s", "demand_hit_rate", "misses_per_token", "copies_per_token")
+        pools = {}
+        for gib in (3, 6, 12, 24):
+            pf = big if gib == 24 else session(gib << 30, abi.STAGE_PREFETCH)[0]
+            idl, _ = session(gib << 30, abi.STAGE_PREFETCH_IDLE)
+            dm, _ = session(gib << 30, None)
+            pools[str(gib)] = {"slots": (gib << 30) // blob,
+                               "with_prefetch": dict({k: pf[k] for k in keys},
+                                                     prefetch_precision=pf["prefetch_precision"]),
+                               "idle_prefetch": dict({k: idl[k] for k in keys},
+                                                     prefetch_skipped=idl["stats"]["prefetch_skipped"]),
+                               "demand_only": {k: dm[k] for k in keys}}
     finally:
         abi.moe_host_free_pinned(host)
         abi.moe_ctx_destroy(ctx)
-    n = steps - warm
-    dem = st["demand_hits"] + st["demand_misses"]
-    return {
+    out = {
         "workload": "expert streaming with the router lookahead: 16 GLM-shaped layers with their "
                     "own routers and Zipf(1.1) biases, x_(l+1) = bf16(x_l + gamma*y_l), decode "
                     "batch 1, the guess for layer l+1 = layer l+1's router on x_l; 4096 routed "
@@ -786,20 +841,12 @@ def run_stream_lookahead(args, lay):
                     "HBM LRU pool" % n_phys,
         "gamma": gamma,
         "gamma_calibration_precision": {str(g): v for g, v in cal.items()},
-        "predictor": {"precision": hit / tot, "recall": hit / tot,
+        "predictor": {"precision": prec, "recall": prec,
                       "note": "k guessed, k actual per layer: precision equals recall"},
-        "tokens_per_s": n / dt,
-        "ms_per_token": 1e3 * dt / n,
-        "demand_hit_rate": st["demand_hits"] / dem if dem else None,
-        "prefetch_precision": (st["prefetch_used"] / st["prefetch_issued"]
-                               if st["prefetch_issued"] else None),
-        "prefetch_coverage": (st["prefetch_used"] / (st["prefetch_used"] + st["demand_misses"])
-                              if st["prefetch_used"] + st["demand_misses"] else None),
-        "h2d_GBs_copy_busy": (st["bytes_copied"] / (st["copy_busy_ms"] * 1e-3) / 1e9
-                              if st["copy_busy_ms"] > 0 else None),
-        "copies_per_token": (st["demand_misses"] + st["prefetch_issued"]) / n,
-        "stats": st,
     }
+    out.update(big)
+    out["by_pool_GiB"] = pools
+    return out
 
 
 class _one_core:

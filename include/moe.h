@@ -237,6 +237,14 @@ moe_status moe_layer_forward_noalloc(const moe_layer_desc *desc, const void *x, 
  * moe_cache_stage(PREFETCH): same lookup for a predicted set, but never waits,
  * never evicts a locked slot, and skips (counted) when no unlocked slot is
  * left; prefetched slots are not locked.
+ * moe_cache_stage(PREFETCH_IDLE): PREFETCH only while the copy engine is idle:
+ * when copies issued earlier are still running on the cache's copy stream, the
+ * whole request is skipped (each id counted in prefetch_skipped, event kind
+ * 8), so a guess never delays a demand copy.  Where one layer computes in far
+ * less time than one expert takes to cross PCIe, streaming is copy-bound and
+ * prefetching wrong guesses only costs copy time; this form prefetches into
+ * the idle gaps alone.  Which requests run depends on timing (the HOST backend
+ * copies synchronously and is never busy: there it equals PREFETCH).
  * moe_cache_release: unlocks the slots of `layer`; before a released slot is
  * refilled, the copy stream waits until the work enqueued on `compute` up to
  * the release has finished (no write-after-read hazard).
@@ -251,6 +259,7 @@ moe_status moe_layer_forward_noalloc(const moe_layer_desc *desc, const void *x, 
 #define MOE_CACHE_BACKEND_HOST   1
 #define MOE_STAGE_DEMAND   0
 #define MOE_STAGE_PREFETCH 1
+#define MOE_STAGE_PREFETCH_IDLE 2
 
 typedef struct moe_cache_desc {
     int32_t device;
@@ -282,7 +291,7 @@ typedef struct moe_cache_stats {
 
 /* One logical cache event (kind: 0 hit, 1 miss, 2 prefetch issued, 3 prefetch
  * already resident, 4 prefetch skipped, 5 eviction, 6 pinned key copied in,
- * 7 pinned key already resident). */
+ * 7 pinned key already resident, 8 prefetch skipped: copy engine busy). */
 typedef struct moe_cache_event {
     int32_t kind, layer, expert, slot;
 } moe_cache_event;

@@ -19,7 +19,7 @@ DT_F32, DT_BF16 = 0, 1
 PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_MX_BF16 = 0, 1, 2, 3
 CACHE_GLOBAL_LRU, CACHE_PER_LAYER_LRU = 0, 1
 CACHE_BACKEND_HIP, CACHE_BACKEND_HOST = 0, 1
-STAGE_DEMAND, STAGE_PREFETCH = 0, 1
+STAGE_DEMAND, STAGE_PREFETCH, STAGE_PREFETCH_IDLE = 0, 1, 2
 NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
 
 _NAMES = {OK: "OK", E_INVAL: "E_INVAL", E_UNSUPPORTED: "E_UNSUPPORTED", E_NOMEM: "E_NOMEM",

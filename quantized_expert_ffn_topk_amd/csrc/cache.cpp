@@ -502,6 +502,22 @@ extern "C" moe_status moe_cache_stage(moe_cache *cache, int32_t layer, const int
                             dev_ptrs_host_out);
     if (mode == MOE_STAGE_PREFETCH)
         return stage_prefetch(cache, layer, ids_host, n);
+    if (mode == MOE_STAGE_PREFETCH_IDLE) {
+        if (hip_backend(cache)) {
+            const hipError_t q = hipStreamQuery(cache->copy);
+            if (q == hipErrorNotReady) {
+                // copies still in flight: a prefetch now would queue behind
+                // them and delay the next demand copies
+                for (int j = 0; j < n; ++j)
+                    emit(cache, 8, layer, ids_host[j], -1);
+                cache->st.prefetch_skipped += n;
+                return MOE_OK;
+            }
+            if (q != hipSuccess)
+                return hip_fail(q, "hipStreamQuery(copy stream)");
+        }
+        return stage_prefetch(cache, layer, ids_host, n);
+    }
     return fail(MOE_E_INVAL, "unknown stage mode %d", mode);
 }
 

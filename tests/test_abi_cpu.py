@@ -205,7 +205,7 @@ class HostCache:
         abi.moe_cache_destroy(self.h)
 
 
-def run_trace(hc, demand, predict):
+def run_trace(hc, demand, predict, mode=abi.STAGE_PREFETCH):
     steps, L_, k = demand.shape
     for t in range(steps):
         for l in range(L_):
@@ -219,7 +219,7 @@ def run_trace(hc, demand, predict):
                     if t + 1 >= steps:
                         abi.moe_cache_release(hc.h, l)
                         continue
-                abi.moe_cache_stage(hc.h, nl, predict[t, l], abi.STAGE_PREFETCH)
+                abi.moe_cache_stage(hc.h, nl, predict[t, l], mode)
             abi.moe_cache_release(hc.h, l)
 
 
@@ -243,6 +243,25 @@ def test_host_cache_log_equals_oracle_sim(orc, cap, per_layer, with_pred):
     for key in st:
         assert stats[key] == st[key], key
     assert stats["bytes_copied"] == 256 * (stats["demand_misses"] + stats["prefetch_issued"])
+
+
+def test_host_cache_idle_prefetch_equals_prefetch(orc):
+    # the host backend copies synchronously, so its copy engine is never busy
+    # and PREFETCH_IDLE takes every request: the same log as PREFETCH and as
+    # the oracle's state machine
+    L_, E, k, steps = 4, 32, 4, 25
+    dem, pred = synth.zipf_trace(11, L_, E, k, steps)
+    hc = HostCache(L_, E, 13, False)
+    try:
+        run_trace(hc, dem, pred, abi.STAGE_PREFETCH_IDLE)
+        log = abi.moe_cache_event_log(hc.h)
+        stats = abi.moe_cache_stats_get(hc.h)
+    finally:
+        hc.close()
+    ev, st = orc.cache_sim(L_, E, k, 13, dem, pred, wrap=True, per_layer=False)
+    assert np.array_equal(log, ev)
+    for key in st:
+        assert stats[key] == st[key], key
 
 
 def test_host_cache_capacity_and_failed_copy():

@@ -54,7 +54,7 @@ class Stack:
         abi.moe_host_free_pinned(self.host)
 
 
-def _run(stk, demand, predict, steps, pins=None):
+def _run(stk, demand, predict, steps, pins=None, mode=abi.STAGE_PREFETCH):
     """The streaming loop: layer l runs through the cache (DEMAND inside the
     forward), then the guess for the next layer is prefetched and layer l is
     released; every output is checked against the resident layer.  pins[t]
@@ -85,10 +85,37 @@ def _run(stk, demand, predict, steps, pins=None):
                     if t + 1 >= steps:
                         abi.moe_cache_release(stk.cache, l)
                         continue
-                abi.moe_cache_stage(stk.cache, nl, predict[t, l], abi.STAGE_PREFETCH)
+                abi.moe_cache_stage(stk.cache, nl, predict[t, l], mode)
             abi.moe_cache_release(stk.cache, l)
     torch.cuda.synchronize()
     return used
+
+
+@pytest.mark.parametrize("n_slots", [7, 12])
+def test_idle_prefetch_keeps_outputs_and_accounts_every_guess(n_slots):
+    # PREFETCH_IDLE: which guesses are copied depends on timing, so the log is
+    # not compared with the oracle; every output still equals the resident
+    # layer's bit for bit (checked in _run), every guessed id is counted once
+    # (issued, already resident or skipped), and the events are the known kinds
+    steps = 5
+    demand, predict = synth.zipf_trace(8, L_, E, K, steps)
+    stk = Stack(n_slots)
+    try:
+        _run(stk, demand, predict, steps, mode=abi.STAGE_PREFETCH_IDLE)
+        log = abi.moe_cache_event_log(stk.cache)
+        stats = abi.moe_cache_stats_get(stk.cache)
+    finally:
+        stk.close()
+    n_guess = (steps * L_ - 1) * K
+    assert stats["prefetch_issued"] + stats["prefetch_resident"] + stats["prefetch_skipped"] == n_guess
+    kinds = set(log[:, 0].tolist())
+    assert kinds <= {0, 1, 2, 3, 4, 5, 8}
+    busy = int((log[:, 0] == 8).sum())
+    assert busy <= stats["prefetch_skipped"]
+    assert stats["bytes_copied"] == stk.blob * (stats["demand_misses"] + stats["prefetch_issued"])
+    print("idle prefetch, %d slots: %d issued, %d resident, %d skipped (%d with the copy engine "
+          "busy)" % (n_slots, stats["prefetch_issued"], stats["prefetch_resident"],
+                     stats["prefetch_skipped"], busy))
 
 
 @pytest.mark.parametrize("n_slots,with_pred", [(6, False), (9, True), (24, True)])
