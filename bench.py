@@ -430,6 +430,36 @@ def run_mx(args):
     return res
 
 
+def hbm_read_probe(mib=1024, reps=5):
+    """A measured HBM read ceiling for this run: `mib` MiB read by the
+    library's streaming-read probe (moe_debug_stream_read: the decode
+    kernels' 16-byte non-temporal loads, 64 KiB per block), event-timed on
+    the launch stream, best of `reps`."""
+    import torch
+    from quantized_expert_ffn_topk_amd import abi
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(7)
+    sink = torch.empty(n >> 16, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    abi.moe_debug_stream_read(src, n, sink, stream)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        abi.moe_debug_stream_read(src, n, sink, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del src, sink
+    torch.cuda.empty_cache()
+    return {"kind": "streaming read of %d MiB with 16-byte non-temporal loads "
+                    "(moe_debug_stream_read)" % mib,
+            "GBs": n / (best * 1e-3) / 1e9}
+
+
 def decode_gemv_roofline(kus, g):
     """Algorithmic bytes and HBM fraction of the one-token gate/up and down
     launches (group size g)."""
@@ -1033,6 +1063,7 @@ def main():
     gemv_us = gu_us + dn_us
     achieved = gemv_bytes / (gemv_us * 1e-6) / 1e9
     traffic = measured_traffic()
+    probe = hbm_read_probe()
     layer_bytes = S * (gu_section_bytes(H, F, G) + dn_section_bytes(H, F, G)) + E * H * 4
     line = {
         "metric": METRIC,
@@ -1066,6 +1097,9 @@ def main():
             "traffic": (traffic["gateup"] + traffic["down"]) if traffic else None,
             "bytes_per_step": gemv_bytes,
             "avg_us": gemv_us,
+            # the same achieved rate against a ceiling measured in this run
+            "probe": probe,
+            "frac_of_probe": achieved / probe["GBs"],
             "per_kernel": {
                 "gateup": {"bytes_per_launch": gu_bytes, "avg_us": gu_us,
                            "achieved": gu_bytes / (gu_us * 1e-6) / 1e9,

@@ -379,6 +379,12 @@ moe_status moe_debug_read(moe_ctx *ctx, int32_t which, void *dst, size_t bytes,
 moe_status moe_debug_project(moe_ctx *ctx, const void *blob, int32_t part,
                              const int8_t *q_in, const float *s_in, int32_t T,
                              float *y, void *stream);
+/* Measurement helper: reads `bytes` of device memory at src (16-byte aligned,
+ * a nonzero multiple of 65536) with the 16-byte non-temporal loads the decode
+ * kernels use for expert weights, 64 KiB per block; sink [bytes/65536]
+ * (device, caller-owned) receives the XOR of the 32-bit words of each 64 KiB
+ * block.  Enqueued on `stream`; E_INVAL on a bad argument, nothing enqueued. */
+moe_status moe_debug_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -115,6 +115,7 @@ def _declare(L):
         "moe_last_error": (C.c_char_p, []),
         "moe_debug_read": (st, [vp, i32, vp, C.c_size_t, vp]),
         "moe_debug_project": (st, [vp, vp, i32, vp, vp, i32, vp, vp]),
+        "moe_debug_stream_read": (st, [vp, C.c_size_t, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -323,3 +324,7 @@ def moe_debug_read(ctx, which, dst, nbytes, stream=None):
 def moe_debug_project(ctx, blob, part, q_in, s_in, T, y, stream=None):
     check(lib().moe_debug_project(ctx, addr(blob), part, addr(q_in), addr(s_in), T, addr(y),
                                   stream_handle(stream)))
+
+
+def moe_debug_stream_read(src, nbytes, sink, stream=None):
+    check(lib().moe_debug_stream_read(addr(src), nbytes, addr(sink), stream_handle(stream)))

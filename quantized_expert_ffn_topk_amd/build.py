@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 HIP_SOURCES = ["kernels_router.hip", "kernels_gemv.hip", "kernels_bs1.hip", "kernels_gemm.hip",
-               "kernels_mx.hip", "noalloc.hip"]
+               "kernels_mx.hip", "noalloc.hip", "kernels_probe.hip"]
 CPP_SOURCES = ["api.cpp", "pack.cpp", "cache.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math", "-Wall",

@@ -339,3 +339,12 @@ def test_host_cache_pin_needs_no_locked_slot_and_valid_usage():
         assert abi.moe_cache_usage_get(hc.h, 32)[[1, 2]].tolist() == [1, 1]
     finally:
         hc.close()
+
+
+def test_stream_read_probe_rejects_bad_arguments_before_any_launch():
+    # every case returns before a kernel would be enqueued
+    for src, n, sink in [(None, 65536, 16), (16, 65536, None), (16, 0, 16), (16, 65536 + 16, 16),
+                         (24, 65536, 16)]:
+        with pytest.raises(abi.MoEError) as ei:
+            abi.moe_debug_stream_read(src, n, sink)
+        assert ei.value.status == abi.E_INVAL
