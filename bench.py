@@ -430,34 +430,41 @@ def run_mx(args):
     return res
 
 
-def hbm_read_probe(mib=1024, reps=5):
-    """A measured HBM read ceiling for this run: `mib` MiB read by the
-    library's streaming-read probe (moe_debug_stream_read: the decode
-    kernels' 16-byte non-temporal loads, 64 KiB per block), event-timed on
-    the launch stream, best of `reps`."""
+def hbm_read_probe(sizes, reps=50):
+    """A measured HBM read ceiling for this run: for each size in `sizes`
+    (bytes, rounded down to 64 KiB), the library's streaming-read probe
+    (moe_debug_stream_read: the decode kernels' 16-byte non-temporal loads,
+    64 KiB per block) reads that many bytes, event-timed on the launch stream
+    and averaged over `reps` launches like the kernels' own times; the ceiling
+    is the bytes over the summed mean times."""
     import torch
     from quantized_expert_ffn_topk_amd import abi
-    n = mib << 20
-    src = torch.empty(n, dtype=torch.uint8, device="cuda")
-    src.fill_(7)
-    sink = torch.empty(n >> 16, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
-    abi.moe_debug_stream_read(src, n, sink, stream)
-    torch.cuda.synchronize()
-    best = None
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        abi.moe_debug_stream_read(src, n, sink, stream)
-        e1.record(stream)
+    tot_b, tot_ms, per = 0, 0.0, []
+    for size in sizes:
+        n = size >> 16 << 16
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src.fill_(7)
+        sink = torch.empty(n >> 16, dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            abi.moe_debug_stream_read(src, n, sink, stream)
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
-        best = ms if best is None else min(best, ms)
-    del src, sink
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            abi.moe_debug_stream_read(src, n, sink, stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / reps
+        per.append({"bytes": n, "avg_us": 1e3 * ms, "GBs": n / (ms * 1e-3) / 1e9})
+        tot_b += n
+        tot_ms += ms
+        del src, sink
     torch.cuda.empty_cache()
-    return {"kind": "streaming read of %d MiB with 16-byte non-temporal loads "
-                    "(moe_debug_stream_read)" % mib,
-            "GBs": n / (best * 1e-3) / 1e9}
+    return {"kind": "streaming read of the same byte counts in launches of the same sizes, "
+                    "16-byte non-temporal loads (moe_debug_stream_read), mean of %d" % reps,
+            "GBs": tot_b / (tot_ms * 1e-3) / 1e9, "launches": per}
 
 
 def decode_gemv_roofline(kus, g):
@@ -1062,8 +1069,8 @@ def main():
     gemv_bytes = gu_bytes + dn_bytes
     gemv_us = gu_us + dn_us
     achieved = gemv_bytes / (gemv_us * 1e-6) / 1e9
+    probe = hbm_read_probe([gu_bytes, dn_bytes])
     traffic = measured_traffic()
-    probe = hbm_read_probe()
     layer_bytes = S * (gu_section_bytes(H, F, G) + dn_section_bytes(H, F, G)) + E * H * 4
     line = {
         "metric": METRIC,
