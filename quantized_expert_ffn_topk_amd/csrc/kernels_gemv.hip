@@ -376,22 +376,32 @@ static int pick_mg(int mg, int K)
     return mg;
 }
 
+// Loads per lane per batch: 12 measured best on the GLM-shaped decode layer
+// (24: fewer, larger batches oversubscribe HBM; 8: too few).  Gate/up never
+// takes more than a wave has (niter = K/256: unused load registers only cost
+// waves; hidden 2048: 39 against 44.5 us on the 16-token tiny layer).  The
+// plain projection takes 8 for K <= 2048 only with 4 or more rows per pass
+// (4-16 tokens: 1-5 % faster; with 1-2 rows per pass 8 measured 38 % slower).
 template <int MG, bool TAIL>
 static void launch_gateup_u(const ProjArgs &a, dim3 grid, size_t lds, float *h, int ldh,
                             const TailArgs &t, int niter, hipStream_t st)
 {
-    // 12 loads of 16 B per lane per batch measured best on the GLM-shaped
-    // decode layer (24: fewer, larger batches oversubscribe HBM; 8: too few)
-    (void)niter;
-    launch(gateup_gemv_kernel<MG, 12, TAIL>, grid, 256, lds, st, a, h, ldh, t);
+    if (niter <= 4)
+        launch(gateup_gemv_kernel<MG, 4, TAIL>, grid, 256, lds, st, a, h, ldh, t);
+    else if (niter <= 8)
+        launch(gateup_gemv_kernel<MG, 8, TAIL>, grid, 256, lds, st, a, h, ldh, t);
+    else
+        launch(gateup_gemv_kernel<MG, 12, TAIL>, grid, 256, lds, st, a, h, ldh, t);
 }
 
 template <int MG, bool TAIL>
 static void launch_proj_u(const ProjArgs &a, dim3 grid, size_t lds, const TailArgs &t, int niter,
                           hipStream_t st)
 {
-    (void)niter;
-    launch(proj_gemv_kernel<MG, 12, TAIL>, grid, 256, lds, st, a, t);
+    if (MG >= 4 && niter <= 8)
+        launch(proj_gemv_kernel<MG, 8, TAIL>, grid, 256, lds, st, a, t);
+    else
+        launch(proj_gemv_kernel<MG, 12, TAIL>, grid, 256, lds, st, a, t);
 }
 
 hipError_t launch_gateup_gemv(const ProjArgs &a, int max_active, int F, int mg, float *h, int ldh,
