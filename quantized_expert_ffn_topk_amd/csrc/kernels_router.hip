@@ -577,13 +577,89 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t *__re
         *n_active = base;
 }
 
+// The same, ballot form: one block of 16 waves; the entries go to LDS once; wave w takes experts w,
+// w + 16, ..., and finds an expert's entries 64 at a time with one ballot
+// (lanes = consecutive entries, so the rows land in token order at the
+// popcount of the lanes below); then one wave compacts the experts with rows
+// in expert order.  Each wave runs ceil(nE/16) * ceil(N/64) ballot steps,
+// where the thread-per-expert form runs N/4 LDS reads per thread: with few
+// experts and many entries this form wins (64 experts, 128 entries: 4.2-4.7
+// against 12.6-13.4 us), with many experts and few entries the other.
+__global__ __launch_bounds__(1024) void permute_small_ballot_kernel(const int32_t *__restrict__ idx, int T,
+                                                            int k, int E, int n_shared,
+                                                            int32_t *__restrict__ cnt,
+                                                            int32_t *__restrict__ list,
+                                                            int list_stride,
+                                                            int32_t *__restrict__ active,
+                                                            int32_t *__restrict__ n_active)
+{
+    __shared__ int s_idx[256];
+    __shared__ int s_cnt[1024 + 1];
+    const int N = T * k, S = k + n_shared, tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const uint64_t below = (1ull << lane) - 1ull;
+    if (tid < 256)
+        s_idx[tid] = tid < N ? idx[tid] : -1;
+    __syncthreads();
+    const int nE = E + n_shared;
+    for (int e = wave; e < nE; e += 16) {
+        int32_t *mine = list + (size_t)e * list_stride;
+        int c = 0;
+        if (e < E) {
+            for (int j0 = 0; j0 < N; j0 += 64) {
+                const int j = j0 + lane;
+                const bool hit = j < N && s_idx[j] == e;
+                const uint64_t bal = __ballot(hit);
+                if (hit) {
+                    // ids repeated within a token (not allowed by the API)
+                    // could give an expert more rows than its list holds:
+                    // extra rows are dropped
+                    const int pos = c + __popcll(bal & below);
+                    if (pos < list_stride) {
+                        const int t = j / k, i = j - t * k;
+                        mine[pos] = t * S + i;
+                    }
+                }
+                c += __popcll(bal);
+            }
+        } else {                                   // the shared expert: every token
+            for (int t = lane; t < T; t += 64)
+                mine[t] = t * S + k;
+            c = T;
+        }
+        if (lane == 0) {
+            cnt[e] = c < list_stride ? c : list_stride;
+            s_cnt[e] = c;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        int na = 0;
+        for (int e0 = 0; e0 < nE; e0 += 64) {
+            const int e = e0 + lane;
+            const bool has = e < nE && s_cnt[e] > 0;
+            const uint64_t bal = __ballot(has);
+            if (has)
+                active[na + __popcll(bal & below)] = e;
+            na += __popcll(bal);
+        }
+        if (lane == 0)
+            *n_active = na;
+    }
+}
+
 hipError_t launch_permute(const int32_t *idx, int T, int k, int E, int n_shared, int32_t *cnt,
                           int32_t *list, int list_stride, int32_t *active, int32_t *n_active,
                           uint32_t *done_counter, hipStream_t st)
 {
     if (T * k <= 256) {
-        launch(permute_small_kernel, 1, 1024, 0, st, idx, T, k, E, n_shared, cnt, list, list_stride,
-               active, n_active);
+        const int N = T * k, nE = E + n_shared;
+        if (((nE + 15) / 16) * ((N + 63) / 64) < N / 4)
+            launch(permute_small_ballot_kernel, 1, 1024, 0, st, idx, T, k, E, n_shared, cnt, list,
+                   list_stride, active, n_active);
+        else
+            launch(permute_small_kernel, 1, 1024, 0, st, idx, T, k, E, n_shared, cnt, list,
+                   list_stride, active, n_active);
         return hipGetLastError();
     }
     launch(permute_kernel, E + n_shared, 256, 0, st, idx, T, k, E, n_shared, cnt, list, list_stride,
