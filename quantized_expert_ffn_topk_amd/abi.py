@@ -10,7 +10,9 @@ import ctypes as C
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmoe.so")
+# MOE_LIB: another build of the same library (an instrumented host build, an
+# A/B variant); the in-tree libmoe.so otherwise
+LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(PKG, "libmoe.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
 
 OK, E_INVAL, E_UNSUPPORTED, E_NOMEM, E_HIP, E_CAPACITY = range(6)
