@@ -34,19 +34,14 @@
 
 namespace moe {
 
-// 16 and 2 bytes read as global-memory loads (generic ones become flat loads,
-// which also count against the LDS wait counter).
+// 16 bytes read as a global-memory load (a generic one becomes a flat load,
+// which also counts against the LDS wait counter).
 typedef unsigned int gu32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint4 gload16(const uint4 *p)
 {
     const gu32x4 v = *(const __attribute__((address_space(1))) gu32x4 *)p;
     return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__device__ __forceinline__ uint16_t gload2(const uint16_t *p)
-{
-    return *(const __attribute__((address_space(1))) uint16_t *)p;
 }
 
 // One batch of U 16-byte weight loads and their fp16 scales.
@@ -58,7 +53,7 @@ __device__ __forceinline__ void bs1_load(const uint4 *__restrict__ wp,
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         wv[u] = load_stream16(wp + (size_t)64 * (j0 + u));
-        sv[u] = gload2(sp + (size_t)sstride * (j0 + u));
+        sv[u] = load_stream2(sp + (size_t)sstride * (j0 + u));
     }
 }
 
@@ -246,7 +241,7 @@ __device__ __forceinline__ void gateup_half(const Bs1Args &a, int ai, int q, uns
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
         wv[j] = gload16(wp + 128 * j);
-        sv[j] = gload2(sp_ + (size_t)(128 >> gs) * j);
+        sv[j] = load_stream2(sp_ + (size_t)(128 >> gs) * j);
     }
     if ((int)threadIdx.x < nx)
         reinterpret_cast<uint4 *>(smem)[threadIdx.x] = xs;
@@ -510,7 +505,7 @@ __device__ __forceinline__ void dnh_load(const uint8_t *blob, const Bs1Args &a, 
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         wv[j] = load_stream16(wp + 128 * j);
-        sv[j] = gload2(sp + (size_t)(128 >> gs) * j);
+        sv[j] = load_stream2(sp + (size_t)(128 >> gs) * j);
     }
 }
 
@@ -564,7 +559,7 @@ __device__ __forceinline__ void down_shared_quarter(const Bs1Args &a, const uint
         for (int jj = 0; jj < 2; ++jj) {
             const int j = 2 * q + jj;
             wv[i][jj] = load_stream16(wp + 128 * j);
-            sv[i][jj] = gload2(sp + (size_t)(128 >> gs) * j);
+            sv[i][jj] = load_stream2(sp + (size_t)(128 >> gs) * j);
         }
     }
     float amax = 0.0f;

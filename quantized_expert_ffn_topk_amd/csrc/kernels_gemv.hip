@@ -40,7 +40,7 @@ __device__ __forceinline__ void load_batch(const uint8_t *__restrict__ wt,
         if (it0 + u < niter) {
             const int c = cb + (it0 + u) * 4 + c4;
             wv[u] = load_stream16(wt + ((size_t)c * 16 + r) * 16);
-            sv[u] = st[(size_t)(c >> gshift) * 16 + r];
+            sv[u] = load_stream2(st + (size_t)(c >> gshift) * 16 + r);
         }
     }
 }
