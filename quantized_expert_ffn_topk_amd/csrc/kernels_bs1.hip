@@ -558,7 +558,10 @@ __device__ __forceinline__ void down_shared_quarter(const Bs1Args &a, const uint
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             const int j = 2 * q + jj;
-            wv[i][jj] = load_stream16(wp + 128 * j);
+            // plain loads: every step reads the shared expert again, so it
+            // may stay in the last-level cache (0.3 us per step faster than
+            // the non-temporal hint in an A/B run)
+            wv[i][jj] = gload16(wp + 128 * j);
             sv[i][jj] = load_stream2(sp + (size_t)(128 >> gs) * j);
         }
     }
