@@ -21,6 +21,8 @@ CASES = [
     (512, 256, 300, 6, 1, 32),     # E > 256: rank-counting top-k
     (256, 256, 40, 15, 1, 64),     # 16 slots: 1024-thread down blocks
     (2048, 1024, 8, 1, 0, 32),     # k = 1
+    (4096, 2048, 64, 8, 1, 64),    # two half tiles per down block, shared expert on quarter waves
+    (8192, 2048, 32, 6, 0, 32),    # hidden at the one-token limit: 16-load gate/up batches, two half tiles
 ]
 
 
