@@ -27,8 +27,8 @@ def expert_map(seed, E, nd):
 
 
 def oracle_threads():
-    # the GPU machine gives one GPU's worth of host CPUs (16); the oracle itself
-    # stays single-threaded per call, independent calls run side by side
+    # at most 16 host threads (one GPU's share of a multi-GPU host); the oracle
+    # itself stays single-threaded per call, independent calls run side by side
     return max(1, min(16, os.cpu_count() or 1))
 
 
