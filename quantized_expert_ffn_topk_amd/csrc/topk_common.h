@@ -64,6 +64,39 @@ __device__ __forceinline__ void wave_sort_sel(double &c, int &ci)
     sort_step<64, 1>(c, ci);
 }
 
+// Merge of sorted runs of R lanes (R = 16 or 32, each in the selection order)
+// into one sorted wave: the caller loads the odd runs reversed, so that every
+// pair of runs forms a bitonic sequence, and the half-cleaner stages from
+// 2R lanes up to 64 finish the sort (11 steps for R = 16, 6 for R = 32,
+// against 21 for a full sort).
+template <int R>
+__device__ __forceinline__ void wave_merge_sel(double &c, int &ci)
+{
+    static_assert(R == 16 || R == 32, "runs of 16 or 32 lanes");
+    if constexpr (R == 16) {
+        sort_step<32, 16>(c, ci);
+        sort_step<32, 8>(c, ci);
+        sort_step<32, 4>(c, ci);
+        sort_step<32, 2>(c, ci);
+        sort_step<32, 1>(c, ci);
+    }
+    sort_step<64, 32>(c, ci);
+    sort_step<64, 16>(c, ci);
+    sort_step<64, 8>(c, ci);
+    sort_step<64, 4>(c, ci);
+    sort_step<64, 2>(c, ci);
+    sort_step<64, 1>(c, ci);
+}
+
+// Index to load lane l's candidate from, for runs of R sorted entries laid
+// out one after another: the odd runs reversed (see wave_merge_sel).
+template <int R>
+__device__ __forceinline__ int merge_src(int l)
+{
+    const int run = l / R, pos = l % R;
+    return (run & 1) ? run * R + (R - 1 - pos) : l;
+}
+
 // Top-k of one token for E <= 64*NW (NW = 4, 8 or 16 waves), k <= KEEP (16 or
 // 32).  Thread e < E holds the biased score c of expert e (NaN already mapped
 // to -inf) and has put its sigmoid score in s_s[e]; other threads hold (-inf,
@@ -88,16 +121,18 @@ __device__ __forceinline__ void topk_select_waves(double c, int ci, const double
         cand_i[wave * KEEP + lane] = ci;
     }
     __syncthreads();
-    // candidates left: KEEP*NW, then KEEP per 64 of them per round
+    // candidates left: KEEP*NW, then KEEP per 64 of them per round; every 64
+    // of them are 64/KEEP sorted runs, merged rather than sorted again
 #pragma unroll
     for (int n = KEEP * NW; n > 64; n = n / 64 * KEEP) {
         const int nw = n / 64;
         double cc = -INFINITY;
         int cci = INT_MAX;
         if (wave < nw) {
-            cc = cand_c[64 * wave + lane];
-            cci = cand_i[64 * wave + lane];
-            wave_sort_sel(cc, cci);
+            const int src = 64 * wave + merge_src<KEEP>(lane);
+            cc = cand_c[src];
+            cci = cand_i[src];
+            wave_merge_sel<KEEP>(cc, cci);
         }
         __syncthreads();
         if (wave < nw && lane < KEEP) {
@@ -113,9 +148,12 @@ __device__ __forceinline__ void topk_select_waves(double c, int ci, const double
         return n;
     }();                                             // at most 64 candidates left
     if (wave == 0) {
-        c = lane < NL ? cand_c[lane] : -INFINITY;
-        ci = lane < NL ? cand_i[lane] : INT_MAX;
-        wave_sort_sel(c, ci);
+        // NL = KEEP * (number of runs): sorted runs of KEEP, padded past NL
+        // with entries that sort last
+        const int src = merge_src<KEEP>(lane);
+        c = lane < NL ? cand_c[src] : -INFINITY;
+        ci = lane < NL ? cand_i[src] : INT_MAX;
+        wave_merge_sel<KEEP>(c, ci);
         if (lane < k) {
             s_idx[lane] = ci;
             sel_s[lane] = s_s[ci];
