@@ -452,10 +452,11 @@ static moe_status router_bs1_enqueue(moe_ctx *c, const void *x, const moe_layer_
     if (c->d.n_shared && !w->shared)
         return fail(MOE_E_INVAL, "shared expert blob is NULL");
     const RouteSmallArgs ra = route_small_args(c, x, 1, w, idx, gw, RS_QUANT);
-    LAUNCH(MOE_PROF_ROUTER, "router launch", launch_router_bs1(ra, c->cs, st));
+    LAUNCH(MOE_PROF_ROUTER, "router launch", launch_router_bs1(ra, st));
     const Bs1Args b = make_bs1(c, w, nullptr, idx, gw, nullptr, false);
     LAUNCH(MOE_PROF_TOPK, "top-k launch",
-           launch_topk_bs1(c->cs, c->d.n_experts, c->d.routed_scale, sel ? w->expert_ptrs : nullptr,
+           launch_topk_bs1(c->logits, w->router_bias, c->d.n_experts, c->d.routed_scale,
+                           sel ? w->expert_ptrs : nullptr,
                            idx, gw, c->sel, b, st));
     return MOE_OK;
 }

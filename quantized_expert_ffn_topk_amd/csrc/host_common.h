@@ -33,7 +33,6 @@ struct moe_ctx {
     float *sh = nullptr;
     float *Y = nullptr;
     const void **sel = nullptr;   // one-token path: blob of each rank
-    double *cs = nullptr;         // one-token path: biased scores and scores [2E]
     // MFMA path: tile work list
     int32_t *tiles = nullptr, *n_tiles = nullptr;
     int max_tiles = 0;
@@ -99,7 +98,6 @@ moe_status ws_plan(moe_ctx *c, Fn &&f)
     WS(sh, T * S, WS_DATA);
     WS(Y, T * S * H, WS_DATA);
     WS(sel, k, WS_DATA);
-    WS(cs, 2 * E, WS_DATA);
     WS(tiles, (size_t)c->max_tiles * 2, WS_DATA);
     WS(n_tiles, 4, WS_DATA);
     if (d.wfmt == MOE_WFMT_MXFP4) {

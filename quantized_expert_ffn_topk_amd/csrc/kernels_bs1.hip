@@ -176,16 +176,27 @@ __global__ __launch_bounds__(128 * KS) void gateup_bs1_kernel(Bs1Args a)
     gateup_pairs<U, 1, KS>(a, blockIdx.x, blockIdx.y, smem);
 }
 
+// Sigmoid score s and biased score c (NaN -> -inf) of expert e from its fp64
+// logit, as the many-token top-k computes them.
+__device__ __forceinline__ double bs1_scores(const double *__restrict__ logits,
+                                             const float *__restrict__ bias, int e, double &s)
+{
+    s = 1.0 / (1.0 + exp(-logits[e]));
+    const double cv = s + (double)bias[e];
+    return (cv != cv) ? -INFINITY : cv;
+}
+
 // ---------------------------------------------------------------------------
 // Second launch of the one-token router (after router_bs1_kernel): block 0
-// selects the top k from the biased scores c and scores s (cs = [c | s]),
-// writes ids, weights and the ranks' blobs.  The other blocks run the shared
+// turns the logits into scores s and biased scores c (one expert per
+// thread), selects the top k, writes ids, weights and the ranks' blobs.  The other blocks run the shared
 // expert's gate/up meanwhile (it needs no routing): block 1 + q takes the tile
 // pair q with K split over 2 waves per tile, so the routed gate/up launch that
 // follows is k slots wide.
 // ---------------------------------------------------------------------------
 template <int U>
-__global__ __launch_bounds__(256) void topk_bs1_kernel(const double *__restrict__ cs, int E,
+__global__ __launch_bounds__(256) void topk_bs1_kernel(const double *__restrict__ logits,
+                                                       const float *__restrict__ bias, int E,
                                                        float r, const void *const *ptrs,
                                                        int32_t *idx_out, float *w_out,
                                                        const void **sel, Bs1Args a)
@@ -202,11 +213,12 @@ __global__ __launch_bounds__(256) void topk_bs1_kernel(const double *__restrict_
     double c = -INFINITY;
     int ci = INT_MAX;
     if (tid < E) {
-        c = cs[tid];
-        s_s[tid] = cs[E + tid];
-        ci = tid;
         if (ptrs)
             s_ptr[tid] = ptrs[tid];
+        double sv;
+        c = bs1_scores(logits, bias, tid, sv);
+        s_s[tid] = sv;
+        ci = tid;
     }
     topk_select_256(c, ci, s_s, a.k, r, idx_out, w_out, s_idx, cand_c, cand_i, sel_s);
     if (ptrs && tid < a.k)
@@ -287,7 +299,8 @@ __device__ __forceinline__ void gateup_half(const Bs1Args &a, int ai, int q, uns
 }
 
 template <int NL>
-__global__ __launch_bounds__(512) void topk_bs1h_kernel(const double *__restrict__ cs, int E,
+__global__ __launch_bounds__(512) void topk_bs1h_kernel(const double *__restrict__ logits,
+                                                        const float *__restrict__ bias, int E,
                                                         float r, const void *const *ptrs,
                                                         int32_t *idx_out, float *w_out,
                                                         const void **sel, Bs1Args a)
@@ -311,11 +324,12 @@ __global__ __launch_bounds__(512) void topk_bs1h_kernel(const double *__restrict
     double c = -INFINITY;
     int ci = INT_MAX;
     if (tid < E) {
-        c = cs[tid];
-        s_s[tid] = cs[E + tid];
-        ci = tid;
         if (ptrs)
             s_ptr[tid] = ptrs[tid];
+        double sv;
+        c = bs1_scores(logits, bias, tid, sv);
+        s_s[tid] = sv;
+        ci = tid;
     }
     topk_select_256(c, ci, s_s, a.k, r, idx_out, w_out, s_idx, cand_c, cand_i, sel_s);
     if (ptrs && tid < a.k)
@@ -803,7 +817,8 @@ hipError_t launch_gateup_bs1(const Bs1Args &a, int slots, hipStream_t st)
     return hipGetLastError();
 }
 
-hipError_t launch_topk_bs1(const double *cs, int E, float r, const void *const *ptrs,
+hipError_t launch_topk_bs1(const double *logits, const float *bias, int E, float r,
+                           const void *const *ptrs,
                            int32_t *idx_out, float *w_out, const void **sel, const Bs1Args &a,
                            hipStream_t st)
 {
@@ -812,22 +827,22 @@ hipError_t launch_topk_bs1(const double *cs, int E, float r, const void *const *
     if (a.n_shared && a.H % 1024 == 0) {
         const int blocks = 1 + a.F / 8;
         switch (a.H >> 10) {
-        case 2: launch(topk_bs1h_kernel<2>, blocks, 512, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); return hipGetLastError();
-        case 4: launch(topk_bs1h_kernel<4>, blocks, 512, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); return hipGetLastError();
-        case 6: launch(topk_bs1h_kernel<6>, blocks, 512, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); return hipGetLastError();
-        case 8: launch(topk_bs1h_kernel<8>, blocks, 512, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); return hipGetLastError();
+        case 2: launch(topk_bs1h_kernel<2>, blocks, 512, lds, st, logits, bias, E, r, ptrs, idx_out, w_out, sel, a); return hipGetLastError();
+        case 4: launch(topk_bs1h_kernel<4>, blocks, 512, lds, st, logits, bias, E, r, ptrs, idx_out, w_out, sel, a); return hipGetLastError();
+        case 6: launch(topk_bs1h_kernel<6>, blocks, 512, lds, st, logits, bias, E, r, ptrs, idx_out, w_out, sel, a); return hipGetLastError();
+        case 8: launch(topk_bs1h_kernel<8>, blocks, 512, lds, st, logits, bias, E, r, ptrs, idx_out, w_out, sel, a); return hipGetLastError();
         default: break;
         }
     }
     const int blocks = 1 + (a.n_shared ? a.F / 16 : 0);
     switch (bs1_u((a.H >> 7) / 2, 16)) {
-    case 16: launch(topk_bs1_kernel<16>, blocks, 256, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); break;
-    case 12: launch(topk_bs1_kernel<12>, blocks, 256, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); break;
-    case 8: launch(topk_bs1_kernel<8>, blocks, 256, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); break;
-    case 6: launch(topk_bs1_kernel<6>, blocks, 256, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); break;
-    case 4: launch(topk_bs1_kernel<4>, blocks, 256, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); break;
-    case 2: launch(topk_bs1_kernel<2>, blocks, 256, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); break;
-    default: launch(topk_bs1_kernel<1>, blocks, 256, lds, st, cs, E, r, ptrs, idx_out, w_out, sel, a); break;
+    case 16: launch(topk_bs1_kernel<16>, blocks, 256, lds, st, logits, bias, E, r, ptrs, idx_out, w_out, sel, a); break;
+    case 12: launch(topk_bs1_kernel<12>, blocks, 256, lds, st, logits, bias, E, r, ptrs, idx_out, w_out, sel, a); break;
+    case 8: launch(topk_bs1_kernel<8>, blocks, 256, lds, st, logits, bias, E, r, ptrs, idx_out, w_out, sel, a); break;
+    case 6: launch(topk_bs1_kernel<6>, blocks, 256, lds, st, logits, bias, E, r, ptrs, idx_out, w_out, sel, a); break;
+    case 4: launch(topk_bs1_kernel<4>, blocks, 256, lds, st, logits, bias, E, r, ptrs, idx_out, w_out, sel, a); break;
+    case 2: launch(topk_bs1_kernel<2>, blocks, 256, lds, st, logits, bias, E, r, ptrs, idx_out, w_out, sel, a); break;
+    default: launch(topk_bs1_kernel<1>, blocks, 256, lds, st, logits, bias, E, r, ptrs, idx_out, w_out, sel, a); break;
     }
     return hipGetLastError();
 }

@@ -1008,11 +1008,11 @@ __global__ __launch_bounds__(256) void route_small_kernel(RouteSmallArgs a)
 // ---------------------------------------------------------------------------
 // One token, first of the two router launches (E <= 256, H <= 8192): block e
 // computes the fp64 logit of expert e (same slices and reduction order as
-// route_small_kernel), its sigmoid score s and biased score c (NaN -> -inf)
-// into cs[e] = c, cs[E + e] = s, and codes its share of the token
-// (quant_share).  topk_bs1_kernel then selects.
+// route_small_kernel) and codes its share of the token (quant_share).  The
+// top-k launch turns the logits into scores, all experts at once (the fp64
+// sigmoid in one thread per block here would delay this launch's end).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void router_bs1_kernel(RouteSmallArgs a, double *__restrict__ cs)
+__global__ __launch_bounds__(256) void router_bs1_kernel(RouteSmallArgs a)
 {
     __shared__ double sred[4];
     __shared__ float samax[4][RS_MAXT];
@@ -1047,21 +1047,15 @@ __global__ __launch_bounds__(256) void router_bs1_kernel(RouteSmallArgs a, doubl
         samax[wave][0] = am;
     }
     __syncthreads();
-    if (tid == 0) {
-        const double L = (sred[0] + sred[1]) + (sred[2] + sred[3]);
-        a.logits[e] = L;
-        const double sv = 1.0 / (1.0 + exp(-L));
-        const double cv = sv + (double)a.bias[e];
-        cs[e] = (cv != cv) ? -INFINITY : cv;
-        cs[a.E + e] = sv;
-    }
+    if (tid == 0)
+        a.logits[e] = (sred[0] + sred[1]) + (sred[2] + sred[3]);
     if (a.flags & RS_QUANT)
         quant_share(a, xv, samax);
 }
 
-hipError_t launch_router_bs1(const RouteSmallArgs &a, double *cs, hipStream_t st)
+hipError_t launch_router_bs1(const RouteSmallArgs &a, hipStream_t st)
 {
-    launch(router_bs1_kernel, a.E, 256, 0, st, a, cs);
+    launch(router_bs1_kernel, a.E, 256, 0, st, a);
     return hipGetLastError();
 }
 

@@ -211,8 +211,9 @@ hipError_t launch_combine(const float *Y, const int32_t *idx, const float *w, in
                           hipStream_t st);
 bool bs1_supported(int H, int F, int k, int n_shared);
 hipError_t launch_gateup_bs1(const Bs1Args &a, int slots, hipStream_t st);
-hipError_t launch_router_bs1(const RouteSmallArgs &a, double *cs, hipStream_t st);
-hipError_t launch_topk_bs1(const double *cs, int E, float r, const void *const *ptrs,
+hipError_t launch_router_bs1(const RouteSmallArgs &a, hipStream_t st);
+hipError_t launch_topk_bs1(const double *logits, const float *bias, int E, float r,
+                           const void *const *ptrs,
                            int32_t *idx_out, float *w_out, const void **sel, const Bs1Args &a,
                            hipStream_t st);
 hipError_t launch_down_bs1(const Bs1Args &a, hipStream_t st);
