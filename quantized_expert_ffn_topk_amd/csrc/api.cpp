@@ -342,6 +342,15 @@ static bool small_path(const moe_ctx *c, int T)
            c->d.hidden <= 8192 && c->d.top_k <= 16 && !use_mfma(c, T);
 }
 
+// Whether all expert blobs of a layer fit the last-level cache (the 256 MiB
+// Infinity Cache of an MI355X): then the few-token projections read them with
+// plain loads and they stay cached from one call to the next.
+static bool experts_fit_llc(const moe_layer_desc &d, const BlobLayout &L)
+{
+    constexpr double kLastLevelCacheBytes = 256.0 * 1024 * 1024;
+    return (double)(d.n_experts + d.n_shared) * (double)L.total <= kLastLevelCacheBytes;
+}
+
 // One token: expert FFN straight from the top-k output (kernels_bs1.hip).
 static bool bs1_path(const moe_ctx *c, int T)
 {
@@ -551,6 +560,7 @@ static moe_status ffn_enqueue(moe_ctx *c, const void *x, int32_t T, const moe_la
     a.ex.ptrs = expert_ptrs;
     a.ex.shared = w->shared;
     a.ex.E = E;
+    a.cached = experts_fit_llc(d, c->L) ? 1 : 0;
     a.rt.active = c->active;
     a.rt.n_active = c->n_active;
     a.rt.cnt = c->cnt;

@@ -29,12 +29,31 @@
 
 namespace moe {
 
-template <int U>
+// One batch of U weight loads and their scales; CACHED: plain loads (the
+// layer's experts fit the last-level cache and stay there between calls: the
+// 16-token tiny layer 188 k -> 195 k tokens/s), else the non-temporal hint
+// (the GLM-shaped layer's experts do not fit: plain loads 8-11 % slower).  A
+// template parameter, not a runtime flag: both load forms in one kernel
+// raised its registers (gate/up 179 VGPRs) and cost a third of the speed.
+template <int U, bool CACHED>
 __device__ __forceinline__ void load_batch(const uint8_t *__restrict__ wt,
                                            const uint16_t *__restrict__ st, int cb, int it0,
-                                           int niter, int c4, int r, int gshift, uint4 (&wv)[U],
-                                           uint16_t (&sv)[U])
+                                           int niter, int c4, int r, int gshift,
+                                           uint4 (&wv)[U], uint16_t (&sv)[U])
 {
+    typedef unsigned int g4 __attribute__((ext_vector_type(4)));
+    if constexpr (CACHED) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (it0 + u < niter) {
+                const int c = cb + (it0 + u) * 4 + c4;
+                const g4 v = *(const __attribute__((address_space(1))) g4 *)(wt + ((size_t)c * 16 + r) * 16);
+                wv[u] = make_uint4(v.x, v.y, v.z, v.w);
+                sv[u] = *(const __attribute__((address_space(1))) uint16_t *)(st + (size_t)(c >> gshift) * 16 + r);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (it0 + u < niter) {
@@ -144,7 +163,7 @@ __device__ __forceinline__ void stage_rows(const ProjArgs &a, const int32_t *lst
 
 // Exact partial sums of tile pair (wt0, wt1) for all passes of MG rows; calls
 // epi(base, mc, part, lsa, lslot) after each pass (part[wave][m][r] in LDS).
-template <int MG, int U, class Epi>
+template <int MG, int U, bool CACHED, class Epi>
 __device__ __forceinline__ void gemv_tile_pair(const ProjArgs &a, const uint8_t *wt0,
                                                const uint8_t *wt1, const uint16_t *st0,
                                                const uint16_t *st1, const int32_t *lst, int n,
@@ -167,7 +186,7 @@ __device__ __forceinline__ void gemv_tile_pair(const ProjArgs &a, const uint8_t 
 
     uint4 wv[U];
     uint16_t sv[U];
-    load_batch<U>(wt, st, cb, 0, niter, c4, r, a.group_shift, wv, sv);   // before staging
+    load_batch<U, CACHED>(wt, st, cb, 0, niter, c4, r, a.group_shift, wv, sv);   // before staging
     for (int base = 0; base < n; base += MG) {
         const int mc = min(MG, n - base);
         stage_rows<MG>(a, lst, base, mc, lq, lsa, lslot);
@@ -178,7 +197,7 @@ __device__ __forceinline__ void gemv_tile_pair(const ProjArgs &a, const uint8_t 
             p[m] = 0.0;
         for (int it0 = 0; it0 < niter; it0 += U) {
             if (base > 0 || it0 > 0)
-                load_batch<U>(wt, st, cb, it0, niter, c4, r, a.group_shift, wv, sv);
+                load_batch<U, CACHED>(wt, st, cb, it0, niter, c4, r, a.group_shift, wv, sv);
             compute_batch<MG, U>(wv, sv, cb, it0, niter, c4, mc, lq, K, p);
         }
 #pragma unroll
@@ -245,7 +264,7 @@ __device__ __forceinline__ void requant_row(const float *__restrict__ hr, int F,
 // SwiGLU is the reading taken for the experts' activation (the pages do not
 // name one; DeepSeek-V3-family experts use it).
 // ---------------------------------------------------------------------------
-template <int MG, int U, bool TAIL>
+template <int MG, int U, bool TAIL, bool CACHED>
 __global__ __launch_bounds__(256) void gateup_gemv_kernel(ProjArgs a, float *__restrict__ h,
                                                           int ldh, TailArgs t)
 {
@@ -263,7 +282,7 @@ __global__ __launch_bounds__(256) void gateup_gemv_kernel(ProjArgs a, float *__r
     const uint16_t *st1 = reinterpret_cast<const uint16_t *>(blob + a.s_off + (size_t)(2 * b + 1) * a.tile_s);
     const int n = a.rt.cnt[e];
     const int32_t *lst = a.rt.list + (size_t)e * a.rt.list_stride;
-    gemv_tile_pair<MG, U>(a, wt0, wt1, st0, st1, lst, n, smem,
+    gemv_tile_pair<MG, U, CACHED>(a, wt0, wt1, st0, st1, lst, n, smem,
                           [&](int, int mc, const double *part, const float *lsa, const int *lslot) {
                               if (threadIdx.x < 16 * mc) {
                                   const int m = threadIdx.x >> 4, rr = threadIdx.x & 15;
@@ -299,7 +318,7 @@ __global__ __launch_bounds__(256) void gateup_gemv_kernel(ProjArgs a, float *__r
 // tile `pair` combines: out[t, n] = Y_shared + sum_i w_i * Y_i (fp64, shared
 // first then rank order, rounded once).
 // ---------------------------------------------------------------------------
-template <int MG, int U, bool TAIL>
+template <int MG, int U, bool TAIL, bool CACHED>
 __global__ __launch_bounds__(256) void proj_gemv_kernel(ProjArgs a, TailArgs t)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -319,7 +338,7 @@ __global__ __launch_bounds__(256) void proj_gemv_kernel(ProjArgs a, TailArgs t)
     const uint16_t *st1 = reinterpret_cast<const uint16_t *>(blob + a.s_off + (size_t)tile1 * a.tile_s);
     const int n = a.rt.cnt[e];
     const int32_t *lst = a.rt.list + (size_t)e * a.rt.list_stride;
-    gemv_tile_pair<MG, U>(a, wt0, wt1, st0, st1, lst, n, smem,
+    gemv_tile_pair<MG, U, CACHED>(a, wt0, wt1, st0, st1, lst, n, smem,
                           [&](int, int mc, const double *part, const float *lsa, const int *lslot) {
                               if (threadIdx.x < 32 * mc) {
                                   const int m = threadIdx.x >> 5, j = (threadIdx.x >> 4) & 1, rr = threadIdx.x & 15;
@@ -382,26 +401,46 @@ static int pick_mg(int mg, int K)
 // waves; hidden 2048: 39 against 44.5 us on the 16-token tiny layer).  The
 // plain projection takes 8 for K <= 2048 only with 4 or more rows per pass
 // (4-16 tokens: 1-5 % faster; with 1-2 rows per pass 8 measured 38 % slower).
+template <int MG, bool TAIL, bool CACHED>
+static void launch_gateup_uc(const ProjArgs &a, dim3 grid, size_t lds, float *h, int ldh,
+                             const TailArgs &t, int niter, hipStream_t st)
+{
+    if (niter <= 4)
+        launch(gateup_gemv_kernel<MG, 4, TAIL, CACHED>, grid, 256, lds, st, a, h, ldh, t);
+    else if (niter <= 8)
+        launch(gateup_gemv_kernel<MG, 8, TAIL, CACHED>, grid, 256, lds, st, a, h, ldh, t);
+    else
+        launch(gateup_gemv_kernel<MG, 12, TAIL, CACHED>, grid, 256, lds, st, a, h, ldh, t);
+}
+
 template <int MG, bool TAIL>
 static void launch_gateup_u(const ProjArgs &a, dim3 grid, size_t lds, float *h, int ldh,
                             const TailArgs &t, int niter, hipStream_t st)
 {
-    if (niter <= 4)
-        launch(gateup_gemv_kernel<MG, 4, TAIL>, grid, 256, lds, st, a, h, ldh, t);
-    else if (niter <= 8)
-        launch(gateup_gemv_kernel<MG, 8, TAIL>, grid, 256, lds, st, a, h, ldh, t);
+    if (a.cached)
+        launch_gateup_uc<MG, TAIL, true>(a, grid, lds, h, ldh, t, niter, st);
     else
-        launch(gateup_gemv_kernel<MG, 12, TAIL>, grid, 256, lds, st, a, h, ldh, t);
+        launch_gateup_uc<MG, TAIL, false>(a, grid, lds, h, ldh, t, niter, st);
+}
+
+template <int MG, bool TAIL, bool CACHED>
+static void launch_proj_uc(const ProjArgs &a, dim3 grid, size_t lds, const TailArgs &t, int niter,
+                           hipStream_t st)
+{
+    if (MG >= 4 && niter <= 8)
+        launch(proj_gemv_kernel<MG, 8, TAIL, CACHED>, grid, 256, lds, st, a, t);
+    else
+        launch(proj_gemv_kernel<MG, 12, TAIL, CACHED>, grid, 256, lds, st, a, t);
 }
 
 template <int MG, bool TAIL>
 static void launch_proj_u(const ProjArgs &a, dim3 grid, size_t lds, const TailArgs &t, int niter,
                           hipStream_t st)
 {
-    if (MG >= 4 && niter <= 8)
-        launch(proj_gemv_kernel<MG, 8, TAIL>, grid, 256, lds, st, a, t);
+    if (a.cached)
+        launch_proj_uc<MG, TAIL, true>(a, grid, lds, t, niter, st);
     else
-        launch(proj_gemv_kernel<MG, 12, TAIL>, grid, 256, lds, st, a, t);
+        launch_proj_uc<MG, TAIL, false>(a, grid, lds, t, niter, st);
 }
 
 hipError_t launch_gateup_gemv(const ProjArgs &a, int max_active, int F, int mg, float *h, int ldh,

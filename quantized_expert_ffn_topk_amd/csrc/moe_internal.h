@@ -93,6 +93,10 @@ struct ProjArgs {
     // output rows: out[slot * ldo + 32*pair + 16*j + r]
     float *out;
     int ldo;
+    // 1: the layer's expert blobs fit the last-level cache, so the GEMV reads
+    // them with plain loads and they stay there between calls; 0: they are
+    // streamed with the non-temporal hint
+    int cached;
 };
 
 // Fused tails of the one-token GEMV path: requantisation of the SwiGLU rows
