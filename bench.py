@@ -164,6 +164,21 @@ def run_decode(args, lay):
             evs[i][1].record(stream)
         torch.cuda.synchronize()
         res["step_us"] = percentiles([1e3 * a.elapsed_time(b) for a, b in evs])
+        # the same steps with the last-level cache flushed before each: a
+        # 512 MiB buffer is written between steps (outside the events), so W_r
+        # and the shared expert, which warm steps may find cached, come from HBM
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=lay.dev)
+        evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_sp)]
+        with torch.cuda.stream(stream):
+            for i in range(n_sp):
+                scratch.fill_(i & 0xff)
+                evc[i][0].record(stream)
+                step(pbase + i)
+                evc[i][1].record(stream)
+        torch.cuda.synchronize()
+        res["step_us_cold"] = percentiles([1e3 * a.elapsed_time(b) for a, b in evc])
+        del scratch
     return res
 
 
@@ -1126,6 +1141,7 @@ def main():
         },
         "kernels_us": {k: round(v, 3) for k, v in res["kernels_us"].items()},
         "step_us_eager": res.get("step_us"),
+        "step_us_eager_cold_llc": res.get("step_us_cold"),
         "eager_tokens_per_s": K / res["eager_s"],
         "profiled_eager_tokens_per_s": K / res["profiled_s"],
         "graph_tokens_per_s": (K / res["graph_s"]) if "graph_s" in res else None,
