@@ -298,6 +298,7 @@ def run_prefill(args, lay):
     ig = idx.clone()
     head_mask = torch.from_numpy(loads >= 256).to(lay.dev)
     idx_head = torch.where(head_mask[ig.long()], ig, torch.full_like(ig, -1))
+    idx_tail = torch.where(head_mask[ig.long()], torch.full_like(ig, -1), ig)
     idx_none = torch.full_like(ig, -1)
 
     def ffn_gemm_us(ix):
@@ -314,6 +315,7 @@ def run_prefill(args, lay):
 
     t_all = ffn_gemm_us(ig)
     t_head = ffn_gemm_us(idx_head)
+    t_tail = ffn_gemm_us(idx_tail)
     t_shared = ffn_gemm_us(idx_none)
     abi.moe_ctx_destroy(ctx)
     rows_head = int(loads[loads >= 256].sum()) + T
@@ -331,6 +333,11 @@ def run_prefill(args, lay):
                  "frac": (ops_row * rows_tail / ((t_all - t_head) * 1e-6) / 1e12 / INT8_PEAK_TOPS
                           if t_all > t_head else None)},
         "shared_only_gemm_us": t_shared,
+        # the tail experts alone (with the shared expert, less the shared
+        # expert alone): a GEMM block costs the same whatever its rows, so
+        # the tail's cost is its block count; in the full call its blocks
+        # also lengthen the last round
+        "tail_alone_gemm_us": t_tail - t_shared,
     }
     return {
         "workload": "same layer, prefill of %d tokens, selection bias skewing loads like "
