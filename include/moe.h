@@ -177,7 +177,12 @@ moe_status moe_expert_ffn(moe_ctx *ctx, const void *x, int32_t T,
  * the cache's copy stream (moe_cache_stage, DEMAND), makes `stream` wait for
  * them and enqueues the FFNs.  The slots stay locked: the caller may then
  * prefetch the next layer (moe_cache_stage, PREFETCH) and must call
- * moe_cache_release(cache, layer, stream).  Source for the
+ * moe_cache_release(cache, layer, stream).  Errors with a cache: E_INVAL
+ * (layer out of range, a cache of another shape or backend, T*k above the
+ * cache's id buffer) before anything is enqueued; E_CAPACITY when the call's
+ * distinct experts need more slots than the layer's partition can give: the
+ * router has then run (idx_out, gate_w_out written), the cache is unchanged
+ * and no slot is locked, so the call can be split into fewer tokens.  Source for the
  * staging: "Guide Complet de Colibri", section "Qu'est-ce que Colibri ?"
  * (experts loaded on demand behind an LRU cache); aifrontierpost tutorial,
  * "Honest limitations" (placement decides speed only: results are identical

@@ -22,7 +22,7 @@ class Stack:
     """L_ layers of E distinct routed experts (+1 shared each) in pinned host
     memory, a cache over them and, for reference, all-resident layers."""
 
-    def __init__(self, n_slots, policy=abi.CACHE_GLOBAL_LRU):
+    def __init__(self, n_slots, policy=abi.CACHE_GLOBAL_LRU, max_tokens=1):
         self.desc = make_desc(H, F, E, K, 1, 32, 2.5)
         self.blob = abi.moe_blob_bytes(self.desc)
         self.experts = [[synth.expert_int4(40 + l, e, H, F, 32) for e in range(E)] for l in range(L_)]
@@ -40,8 +40,8 @@ class Stack:
         self.cache = abi.moe_cache_create(cd)
         abi.moe_cache_log_enable(self.cache, True)
         self.ref = [Layer(self.desc, self.Wr[l], np.zeros(E, np.float32), self.experts[l],
-                          self.shared[l], max_tokens=1) for l in range(L_)]
-        self.ctx = abi.moe_ctx_create(0, self.desc, 1)
+                          self.shared[l], max_tokens=max_tokens) for l in range(L_)]
+        self.ctx = abi.moe_ctx_create(0, self.desc, max_tokens)
         self.bias = torch.zeros(E, dtype=torch.float32, device="cuda")
         self.wts = [abi.moe_layer_weights(self.ref[l].Wr.data_ptr(), self.bias.data_ptr(), None,
                                           self.ref[l].shared_blob.data_ptr()) for l in range(L_)]
@@ -225,3 +225,58 @@ def test_hot_store_pins_equal_oracle_and_keep_placement_invariance(n_slots, n_pi
     assert stats["pinned"] == min(n_pin, n_slots - K)
     assert stats["bytes_copied"] == stk.blob * (stats["demand_misses"] + stats["prefetch_issued"] +
                                                 stats["pin_fills"])
+
+
+def test_multi_token_calls_through_the_cache_equal_resident_layers():
+    # three tokens per call (the few-token GEMV path reading the slots): the
+    # cache stages every distinct expert of the call, the outputs equal the
+    # all-resident layer's bit for bit; a call needing more slots than the
+    # pool has fails with E_CAPACITY, leaves the cache as it was, and a
+    # one-token call goes through afterwards
+    T = 3
+    stk = Stack(16, max_tokens=T)
+    small = Stack(6, max_tokens=T)
+    try:
+        idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+        gw = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        for t in range(3):
+            for l in range(L_):
+                x = stk.ref[l].x_tensor(synth.activations(800 + t * L_ + l, T, H))
+                abi.moe_layer_forward(stk.ctx, x, T, stk.wts[l], stk.cache, l, idx, gw, out)
+                ri, rw, ro = stk.ref[l].forward(x)
+                torch.cuda.synchronize()
+                assert np.array_equal(idx.cpu().numpy(), ri.cpu().numpy()), (t, l)
+                assert torch.equal(gw.view(torch.int32), rw.view(torch.int32)), (t, l)
+                assert torch.equal(out.view(torch.int32), ro.view(torch.int32)), (t, l)
+                abi.moe_cache_release(stk.cache, l)
+        # six slots: a call whose three tokens pick more than six experts
+        failed = 0
+        for s_ in range(6):
+            x = small.ref[0].x_tensor(synth.activations(900 + s_, T, H))
+            ri, _, _ = small.ref[0].forward(x)
+            torch.cuda.synchronize()
+            need = len(set(ri.cpu().numpy().ravel().tolist()))
+            before = abi.moe_cache_stats_get(small.cache)
+            if need > 6:
+                with pytest.raises(abi.MoEError) as ei:
+                    abi.moe_layer_forward(small.ctx, x, T, small.wts[0], small.cache, 0, idx, gw, out)
+                assert ei.value.status == abi.E_CAPACITY
+                assert abi.moe_cache_stats_get(small.cache)["bytes_copied"] == before["bytes_copied"]
+                failed += 1
+            else:
+                abi.moe_layer_forward(small.ctx, x, T, small.wts[0], small.cache, 0, idx, gw, out)
+                abi.moe_cache_release(small.cache, 0)
+        assert failed > 0
+        one_i = torch.empty((1, K), dtype=torch.int32, device="cuda")
+        one_w = torch.empty((1, K), dtype=torch.float32, device="cuda")
+        one_o = torch.empty((1, H), dtype=torch.float32, device="cuda")
+        x1 = small.ref[0].x_tensor(synth.activations(950, 1, H))
+        abi.moe_layer_forward(small.ctx, x1, 1, small.wts[0], small.cache, 0, one_i, one_w, one_o)
+        ri, rw, ro = small.ref[0].forward(x1)
+        torch.cuda.synchronize()
+        assert torch.equal(one_o.view(torch.int32), ro.view(torch.int32))
+        abi.moe_cache_release(small.cache, 0)
+    finally:
+        stk.close()
+        small.close()
