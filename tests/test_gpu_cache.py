@@ -280,3 +280,54 @@ def test_multi_token_calls_through_the_cache_equal_resident_layers():
     finally:
         stk.close()
         small.close()
+
+
+def test_mxfp4_layer_through_the_cache_equals_resident():
+    # MXFP4 blobs staged like int4 ones: one- and two-token calls through the
+    # cache give the resident layer's bits (same kernels on the same bytes,
+    # only the placement differs)
+    from quantized_expert_ffn_topk_amd.layer import pack_mxfp4
+    Tm = 2
+    desc = make_desc(H, F, E, K, 1, 32, 1.0, abi.WFMT_MXFP4)
+    blob = abi.moe_blob_bytes(desc)
+    experts = [synth.expert_mxfp4(60, e, H, F) for e in range(E)]
+    shared = synth.expert_mxfp4(60, -1, H, F)
+    Wr, _ = synth.router_weights(60, E, H)
+    bias = synth.uniform_bias(60, E)
+    host = abi.moe_host_alloc_pinned(E * blob)
+    ref = None
+    cache = None
+    ctx = None
+    try:
+        base = np.ctypeslib.as_array(C.cast(host, C.POINTER(C.c_uint8)), shape=(E * blob,))
+        for e in range(E):
+            base[e * blob:(e + 1) * blob] = pack_mxfp4(desc, experts[e])
+        ptrs = (C.c_void_p * E)(*[host + e * blob for e in range(E)])
+        cd = abi.moe_cache_desc(0, 1, E, blob, 10 * blob, C.addressof(ptrs), abi.CACHE_GLOBAL_LRU,
+                                abi.CACHE_BACKEND_HIP)
+        cache = abi.moe_cache_create(cd)
+        ref = Layer(desc, Wr, bias, experts, shared, max_tokens=Tm)
+        ctx = abi.moe_ctx_create(0, desc, Tm)
+        bz = torch.from_numpy(bias).to("cuda")
+        wts = abi.moe_layer_weights(ref.Wr.data_ptr(), bz.data_ptr(), None, ref.shared_blob.data_ptr())
+        for T in (1, 2):
+            idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+            gw = torch.empty((T, K), dtype=torch.float32, device="cuda")
+            out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+            for s_ in range(4):
+                x = ref.x_tensor(synth.activations(700 + 10 * T + s_, T, H))
+                abi.moe_layer_forward(ctx, x, T, wts, cache, 0, idx, gw, out)
+                ri, rw, ro = ref.forward(x)
+                torch.cuda.synchronize()
+                assert np.array_equal(idx.cpu().numpy(), ri.cpu().numpy()), (T, s_)
+                assert torch.equal(out.view(torch.int32), ro.view(torch.int32)), (T, s_)
+                abi.moe_cache_release(cache, 0)
+        assert abi.moe_cache_stats_get(cache)["bytes_copied"] > 0
+    finally:
+        if ctx:
+            abi.moe_ctx_destroy(ctx)
+        if cache:
+            abi.moe_cache_destroy(cache)
+        if ref:
+            ref.close()
+        abi.moe_host_free_pinned(host)
