@@ -660,6 +660,8 @@ def run_stream(args, lay, W):
         dt_hot, st_hot = stream_pass(args.stream_pins)
         dt_dm, st_dm = stream_pass(0, None)
         dt_id, st_id = stream_pass(0, abi.STAGE_PREFETCH_IDLE)
+        dt_hd, st_hd = stream_pass(args.stream_pins, None)
+        dt_hi, st_hi = stream_pass(args.stream_pins, abi.STAGE_PREFETCH_IDLE)
 
         # the same layer calls with every expert resident (the layer's own 256
         # device blobs, no cache) and the same host synchronisation on the
@@ -751,6 +753,26 @@ def run_stream(args, lay, W):
             "misses_per_token": st_dm["demand_misses"] / n,
             "copies_per_token": st_dm["demand_misses"] / n,
             "stats": st_dm,
+        },
+        "hot_store_demand_only": {
+            "note": "the hot-store as above, without the prefetch calls",
+            "tokens_per_s": n / dt_hd,
+            "demand_hit_rate": st_hd["demand_hits"] / (st_hd["demand_hits"] +
+                                                       st_hd["demand_misses"]),
+            "misses_per_token": st_hd["demand_misses"] / n,
+            "copies_per_token": (st_hd["demand_misses"] + st_hd["pin_fills"]) / n,
+            "stats": st_hd,
+        },
+        "hot_store_idle_prefetch": {
+            "note": "the hot-store as above, the guess prefetched only while the copy engine "
+                    "is idle",
+            "tokens_per_s": n / dt_hi,
+            "demand_hit_rate": st_hi["demand_hits"] / (st_hi["demand_hits"] +
+                                                       st_hi["demand_misses"]),
+            "misses_per_token": st_hi["demand_misses"] / n,
+            "copies_per_token": (st_hi["demand_misses"] + st_hi["prefetch_issued"] +
+                                 st_hi["pin_fills"]) / n,
+            "stats": st_hi,
         },
         "idle_prefetch": {
             "note": "the same trace and pool, the guess prefetched only while the copy engine "
