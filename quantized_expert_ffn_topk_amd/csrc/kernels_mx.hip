@@ -37,7 +37,7 @@
 //
 // Work list: tiles of 16 rows of one expert (mx_tiles); a block covers one row
 // tile and 4 TPW weight tiles (4 waves x TPW tiles of 16 rows; TPW = 8 for
-// gate/up, 4 for down).
+// gate/up, 4 or 2 with few row tiles, and 4 for down).
 //   gate/up: waves hold the gate and up tiles of TPW/2 row pairs; the epilogue is
 //            h = bf16(fp32(G/(1+exp(-G)) * U)) with G, U the fp32 projections;
 //            the h rows are split like the activations before the down launch.
@@ -204,7 +204,7 @@ __device__ __forceinline__ void mx_block_coords(int mt_max, int *nb, int *mt)
 // MXMMA: the MX MFMA on the split activations; otherwise the weights widened
 // to exact bf16 (v_cvt_scalef32_pk_bf16_fp4) against the bf16 rows on
 // v_mfma_f32_16x16x32_bf16 (exact products, plain fp32 accumulation).
-template <bool GATEUP, int TPW, bool MXMMA>
+template <bool GATEUP, int TPW, bool MXMMA, int UNR>
 __global__ __launch_bounds__(256) void mx_proj_kernel(MxArgs a, const int2 *__restrict__ tiles,
                                                       const int32_t *__restrict__ n_tiles,
                                                       int mt_max, int n_groups)
@@ -262,14 +262,26 @@ __global__ __launch_bounds__(256) void mx_proj_kernel(MxArgs a, const int2 *__re
     // 16-31: chunk c0 + 2 + g/2, same inputs; its scale: chunk c0 + g
     const int ao0 = (g >> 1) * 32 + (g & 1) * 16, ao1 = ao0 + 64;
     const int KC = a.K >> 5;
-    for (int c0 = 0; c0 < KC; c0 += 4) {
-        uint4 w[TPW];
-        uint32_t s8[TPW];
+    // UNR steps of 4 chunks per pass, all their weight loads issued first:
+    // with few rows (one-token decode) the weight tiles are few and each
+    // wave's 1 KiB per step would leave the memory system idle
+    for (int cu = 0; cu < KC; cu += 4 * UNR) {
+    uint4 wu[UNR][TPW];
+    uint32_t su[UNR][TPW];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-            w[t] = load_stream16(wt[t] + (size_t)c0 * 16);   // 1 KiB per wave: chunks c0..c0+3, 16 rows
-            s8[t] = st[t][(size_t)c0 * 16];
+            const int c0 = cu + 4 * u;
+            wu[u][t] = load_stream16(wt[t] + (size_t)c0 * 16);   // 1 KiB per wave: chunks c0..c0+3, 16 rows
+            su[u][t] = st[t][(size_t)c0 * 16];
         }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+        const int c0 = cu + 4 * u;
+        const uint4 (&w)[TPW] = wu[u];
+        const uint32_t (&s8)[TPW] = su[u];
         if (MXMMA) {
             uint4 h0 = {}, h1 = {}, l0 = {}, l1 = {};
             int sh = 127, sl = 127;
@@ -314,6 +326,7 @@ __global__ __launch_bounds__(256) void mx_proj_kernel(MxArgs a, const int2 *__re
             }
         }
     }
+    }
 
     // result register i: activation row 4g + i of the tile, weight row r
 #pragma unroll
@@ -355,6 +368,18 @@ size_t mx_max_tiles(int T, int E, int n_shared, int S)
 static int grid8(int n)
 {
     return (n + 7) & ~7;
+}
+
+template <bool GATEUP, int TPW, int UNR>
+static hipError_t mx_launch(bool mxmma, int mt_max, int ng, const MxArgs &a, const int2 *tl,
+                            const int32_t *n_tiles, hipStream_t st)
+{
+    const dim3 grid(grid8(mt_max * ng));
+    if (mxmma)
+        launch(mx_proj_kernel<GATEUP, TPW, true, UNR>, grid, 256, 0, st, a, tl, n_tiles, mt_max, ng);
+    else
+        launch(mx_proj_kernel<GATEUP, TPW, false, UNR>, grid, 256, 0, st, a, tl, n_tiles, mt_max, ng);
+    return hipGetLastError();
 }
 
 moe_status mx_ffn_enqueue(moe_ctx *c, const void *x, int T, const moe_layer_weights *w,
@@ -410,20 +435,22 @@ moe_status mx_ffn_enqueue(moe_ctx *c, const void *x, int T, const moe_layer_weig
     a.n_wtiles = F / 8;
     a.out = c->hb;
     a.ldo = F;
+    // Weight tiles per wave (TPW) and steps of loads issued ahead (UNR) by the
+    // number of row tiles: with few (decode) the waves are few and each
+    // holds few bytes in flight, so loads go several steps ahead.  Measured on
+    // hidden 7168 / FFN 2048 (routed gate/up of a one-token step 67 -> 39 us,
+    // two tokens 70 -> 63 us); from about 3 tokens on, 8 tiles per wave one
+    // step ahead is as fast or faster.  Deeper load queues made the down
+    // launch slower at every size tried, so it keeps 4 tiles per wave (8 ran
+    // ~2 % slower: the down blocks are shorter, K = F).
+    const bool ahead = (H >> 5) % 16 == 0;
     {
-        // 8 weight tiles per wave for gate/up (4 ran the same), 4 for down
-        // (8 ran ~2 % slower: the down blocks are shorter, K = F)
-        const int ng = (a.n_wtiles + 4 * 8 - 1) / (4 * 8);
-        if (mxmma)
-            MX_LAUNCH(MOE_PROF_GATEUP, "gate/up launch",
-                      (launch(mx_proj_kernel<true, 8, true>, grid8(mt_max * ng), 256, 0, st, a, tl,
-                              c->n_tiles, mt_max, ng),
-                       hipGetLastError()));
-        else
-            MX_LAUNCH(MOE_PROF_GATEUP, "gate/up launch",
-                      (launch(mx_proj_kernel<true, 8, false>, grid8(mt_max * ng), 256, 0, st, a, tl,
-                              c->n_tiles, mt_max, ng),
-                       hipGetLastError()));
+        const int tpw = (ahead && mt_max <= 12) ? 4 : (ahead && mt_max <= 24) ? 2 : 8;
+        const int ng = (a.n_wtiles + 4 * tpw - 1) / (4 * tpw);
+        MX_LAUNCH(MOE_PROF_GATEUP, "gate/up launch",
+                  (tpw == 4   ? mx_launch<true, 4, 4>(mxmma, mt_max, ng, a, tl, c->n_tiles, st)
+                   : tpw == 2 ? mx_launch<true, 2, 4>(mxmma, mt_max, ng, a, tl, c->n_tiles, st)
+                              : mx_launch<true, 8, 1>(mxmma, mt_max, ng, a, tl, c->n_tiles, st)));
     }
     // the SwiGLU rows split the same way, then down -> Y [T*S, H]
     if (mxmma)
@@ -441,17 +468,9 @@ moe_status mx_ffn_enqueue(moe_ctx *c, const void *x, int T, const moe_layer_weig
     a.out = c->Y;
     a.ldo = H;
     {
-        const int ng = (a.n_wtiles + 4 * 4 - 1) / (4 * 4);
-        if (mxmma)
-            MX_LAUNCH(MOE_PROF_DOWN, "down launch",
-                      (launch(mx_proj_kernel<false, 4, true>, grid8(mt_max * ng), 256, 0, st, a, tl,
-                              c->n_tiles, mt_max, ng),
-                       hipGetLastError()));
-        else
-            MX_LAUNCH(MOE_PROF_DOWN, "down launch",
-                      (launch(mx_proj_kernel<false, 4, false>, grid8(mt_max * ng), 256, 0, st, a, tl,
-                              c->n_tiles, mt_max, ng),
-                       hipGetLastError()));
+        const int ng = (a.n_wtiles + 15) / 16;
+        MX_LAUNCH(MOE_PROF_DOWN, "down launch",
+                  (mx_launch<false, 4, 1>(mxmma, mt_max, ng, a, tl, c->n_tiles, st)));
     }
     MX_LAUNCH(MOE_PROF_COMBINE, "combine launch",
               launch_combine(c->Y, idx, gw, T, k, E, d.n_shared, H, out, d.out_dtype, st));

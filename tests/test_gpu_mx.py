@@ -66,6 +66,50 @@ def test_mx_layer_matches_oracle(T, shared, path):
     lay.close()
 
 
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("T", [1, 2, 4])
+def test_mx_decode_rows_take_the_few_row_kernels(T, path):
+    # hidden a multiple of 512, top-8 + shared: one token (10 row tiles) runs
+    # gate/up with 4 weight tiles per wave and two tokens (19) with 2, four
+    # steps of loads ahead; four tokens (28) the many-row kernel; against the
+    # oracle at the same bar
+    c = MxCase(35, T, 2048, 1024, 24, 8, 1, r=1.0, n_distinct=4)
+    lay = c.layer(path=path)
+    idx, w, out = lay.forward(lay.x_tensor(c.x))
+    torch.cuda.synchronize()
+    idx_o, w_o, out_o = c.oracle_layer()
+    _, _, _, _, ch = oracle.router(c.x, c.Wr, c.b, c.k, c.r, want=True)
+    check_routing(idx.cpu().numpy(), w.cpu().numpy(), idx_o, w_o, ch)
+    e = _check_mx_out(out.cpu().numpy(), out_o)
+    print("mx decode T=%d path %d: max rel err %.3g" % (T, path, e))
+    lay.close()
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_mx_few_row_kernels_equal_many_row_kernels(path):
+    # the expert FFN of one token alone and of two tokens (few-row gate/up
+    # kernels) and of the same tokens among 70 (many-row kernel), with the
+    # routing given: the same bits, since each output's MFMA sums run over the
+    # same steps in the same order
+    T, H = 70, 2048
+    c = MxCase(36, T, H, 1024, 24, 8, 1, r=1.0, n_distinct=4)
+    lay = c.layer(path=path)
+    x = lay.x_tensor(c.x)
+    idx, w, _ = lay.forward(x)
+    torch.cuda.synchronize()
+    out_all = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    abi.moe_expert_ffn(lay.ctx, x, T, lay.weights, idx, w, out_all)
+    for rows in ([0], [37], [5, 61]):
+        sel = torch.tensor(rows, device="cuda")
+        xs, ids, ws = (v.index_select(0, sel).contiguous() for v in (x, idx, w))
+        out_few = torch.empty((len(rows), H), dtype=torch.float32, device="cuda")
+        abi.moe_expert_ffn(lay.ctx, xs, len(rows), lay.weights, ids, ws, out_few)
+        torch.cuda.synchronize()
+        for j, t in enumerate(rows):
+            assert torch.equal(out_few[j].view(torch.int32), out_all[t].view(torch.int32)), (rows, t)
+    lay.close()
+
+
 def test_mx_swiglu_rows_match_oracle_bf16_path():
     # exact bf16 products, fp32 sums: the bf16 h rows equal the oracle's except
     # where the fp32 projection sits at a bf16 rounding boundary (then one bf16
