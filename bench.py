@@ -435,7 +435,43 @@ def run_mx(args):
             "kernels_us": {k: round(v, 2) for k, v in kus.items()},
         }
 
+    idx1, w1, out1 = lay._outs(1)
+
+    def call1(i):
+        j = i % (4 * Tm)
+        abi.moe_layer_forward(lay.ctx, xs[j // Tm][j % Tm:j % Tm + 1], 1, lay.weights, None, 0,
+                              idx1, w1, out1, sh)
+
+    def measure_decode(path):
+        # one token per call: the routed + shared experts' bytes (9 blobs) per step
+        lay.set_path(path)
+        for i in range(10):
+            call1(i)
+        torch.cuda.synchronize()
+        n = 5 * args.mx_calls
+        t0 = time.perf_counter()
+        for i in range(n):
+            call1(i)
+        stream.synchronize()
+        dt = (time.perf_counter() - t0) / n
+        abi.moe_ctx_profile(lay.ctx, True)
+        abi.moe_ctx_profile_read(lay.ctx)
+        for i in range(n):
+            call1(i)
+        torch.cuda.synchronize()
+        prof = abi.moe_ctx_profile_read(lay.ctx)
+        abi.moe_ctx_profile(lay.ctx, False)
+        kus = {k: 1e3 * v[0] / v[1] for k, v in prof.items() if v[1]}
+        ffn_us = kus.get("gateup", 0.0) + kus.get("down", 0.0)
+        nb = (K_TOP + 1) * blob
+        return {"tokens_per_s": 1.0 / dt, "us_per_step": 1e6 * dt,
+                "expert_bytes_per_step": nb,
+                "expert_ffn_GBs": nb / (ffn_us * 1e-6) / 1e9 if ffn_us else None,
+                "kernels_us": {k: round(v, 2) for k, v in kus.items()}}
+
     res = measure(abi.PATH_AUTO)
+    res["decode_one_token"] = measure_decode(abi.PATH_AUTO)
+    res["decode_one_token"]["bf16_mfma_path"] = measure_decode(abi.PATH_MX_BF16)
     if res["mfma"]["TFLOPs"] is not None:
         res["mfma"]["peak_TFLOPs"] = MFMA_PEAK_TFLOPS["fp8"]
         res["mfma"]["frac"] = res["mfma"]["TFLOPs"] / MFMA_PEAK_TFLOPS["fp8"]
