@@ -22,6 +22,7 @@
 // block, keeping that block in its own L2.
 #include "device_common.h"
 #include "host_common.h"
+#include "permute_common.h"
 
 namespace moe {
 
@@ -54,35 +55,14 @@ static int tiles_bound(const moe_ctx *c, int T)
     return (T * c->S + MT - 1) / MT + busy;
 }
 
-// ---------------------------------------------------------------------------
-// Tile list: for experts 0..n_exp-1 in order, ceil(cnt/mt) tiles (e, m0).
-// One block of 1024 threads; n_exp <= 2048.
-// ---------------------------------------------------------------------------
+// Tile list (row_tiles_block): for experts 0..n_exp-1 in order,
+// ceil(cnt/mt) tiles (e, m0); one block of 1024 threads, n_exp <= 2048.
 __global__ __launch_bounds__(1024) void mfma_tiles_kernel(const int32_t *__restrict__ cnt,
                                                           int n_exp, int mt,
                                                           int2 *__restrict__ tiles,
                                                           int32_t *__restrict__ n_tiles)
 {
-    __shared__ int sc[1024];
-    const int t = threadIdx.x;
-    const int e0 = 2 * t, e1 = 2 * t + 1;
-    const int c0 = e0 < n_exp ? (cnt[e0] + mt - 1) / mt : 0;
-    const int c1 = e1 < n_exp ? (cnt[e1] + mt - 1) / mt : 0;
-    sc[t] = c0 + c1;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        int v = (t >= off) ? sc[t - off] : 0;
-        __syncthreads();
-        sc[t] += v;
-        __syncthreads();
-    }
-    int base = sc[t] - c0 - c1;
-    for (int j = 0; j < c0; ++j)
-        tiles[base + j] = make_int2(e0, j * mt);
-    for (int j = 0; j < c1; ++j)
-        tiles[base + c0 + j] = make_int2(e1, j * mt);
-    if (t == 1023)
-        *n_tiles = sc[1023];
+    row_tiles_block(cnt, n_exp, mt, tiles, n_tiles);
 }
 
 hipError_t launch_mfma_tiles(moe_ctx *c, int T, hipStream_t st)

@@ -44,6 +44,7 @@
 //   down   : Y[slot, n] in fp32, combined afterwards by combine_kernel.
 #include "device_common.h"
 #include "host_common.h"
+#include "permute_common.h"
 
 namespace moe {
 
@@ -71,16 +72,11 @@ struct MxArgs {
 // bf16 rows -> two E4M3 parts with E8M0 scales per 32 (see the file header).
 // One thread per (row, 32 inputs).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void split_fp8_kernel(const uint16_t *__restrict__ x, int rows,
-                                                        int K, uint8_t *__restrict__ hi,
-                                                        uint8_t *__restrict__ lo,
-                                                        uint8_t *__restrict__ e_hi,
-                                                        uint8_t *__restrict__ e_lo)
+__device__ __forceinline__ void split_fp8_group(const uint16_t *__restrict__ x, long i,
+                                                uint8_t *__restrict__ hi, uint8_t *__restrict__ lo,
+                                                uint8_t *__restrict__ e_hi,
+                                                uint8_t *__restrict__ e_lo)
 {
-    const int nb = K >> 5;
-    const long i = (long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (long)rows * nb)
-        return;
     const uint4 *src = reinterpret_cast<const uint4 *>(x + i * 32);
     uint4 v[4];
 #pragma unroll
@@ -135,6 +131,45 @@ __global__ __launch_bounds__(256) void split_fp8_kernel(const uint16_t *__restri
     dl[1] = make_uint4(pl[4], pl[5], pl[6], pl[7]);
     e_hi[i] = (uint8_t)(X + 127);
     e_lo[i] = (uint8_t)(Xl + 127);
+}
+
+__global__ __launch_bounds__(256) void split_fp8_kernel(const uint16_t *__restrict__ x, int rows,
+                                                        int K, uint8_t *__restrict__ hi,
+                                                        uint8_t *__restrict__ lo,
+                                                        uint8_t *__restrict__ e_hi,
+                                                        uint8_t *__restrict__ e_lo)
+{
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i < (long)rows * (K >> 5))
+        split_fp8_group(x, i, hi, lo, e_hi, e_lo);
+}
+
+// A few tokens (at most 256 routing entries) in one launch: block 0 runs the
+// routing permutation and then the row tile list over the counts it has just
+// written (the block barrier makes the block's global writes visible to the
+// block), the other blocks split the tokens' bf16 rows (rows = 0 on the
+// bf16-MFMA path).  Saves two launches of a decode step.
+template <bool BALLOT>
+__global__ __launch_bounds__(1024) void mx_prep_small_kernel(
+    const int32_t *__restrict__ idx, int T, int k, int E, int n_shared, int32_t *__restrict__ cnt,
+    int32_t *__restrict__ list, int list_stride, int32_t *__restrict__ active,
+    int32_t *__restrict__ n_active, int mt, int2 *__restrict__ tiles, int32_t *__restrict__ n_tiles,
+    const uint16_t *__restrict__ x, int rows, int K, uint8_t *__restrict__ hi,
+    uint8_t *__restrict__ lo, uint8_t *__restrict__ e_hi, uint8_t *__restrict__ e_lo)
+{
+    if (blockIdx.x == 0) {
+        if (BALLOT)
+            permute_small_ballot_block(idx, T, k, E, n_shared, cnt, list, list_stride, active,
+                                       n_active);
+        else
+            permute_small_block(idx, T, k, E, n_shared, cnt, list, list_stride, active, n_active);
+        __syncthreads();
+        row_tiles_block(cnt, E + n_shared, mt, tiles, n_tiles);
+        return;
+    }
+    const long i = (long)(blockIdx.x - 1) * 1024 + threadIdx.x;
+    if (i < (long)rows * (K >> 5))
+        split_fp8_group(x, i, hi, lo, e_hi, e_lo);
 }
 
 hipError_t launch_split_fp8(const uint16_t *x, int rows, int K, uint8_t *hi, uint8_t *lo,
@@ -365,6 +400,26 @@ size_t mx_max_tiles(int T, int E, int n_shared, int S)
     return (size_t)T * S / MX_MT + 1 + (size_t)E + (size_t)n_shared;
 }
 
+static hipError_t launch_mx_prep_small(const int32_t *idx, int T, int k, int E, int n_shared,
+                                       moe_ctx *c, int mt, const uint16_t *x, int rows, int K,
+                                       hipStream_t st)
+{
+    const long n = (long)rows * (K >> 5);
+    const int grid = 1 + (int)((n + 1023) / 1024);
+    const int N = T * k, nE = E + n_shared;
+    int2 *tl = reinterpret_cast<int2 *>(c->tiles);
+    // the permutation form launch_permute picks for these sizes
+    if (((nE + 15) / 16) * ((N + 63) / 64) < N / 4)
+        launch(mx_prep_small_kernel<true>, grid, 1024, 0, st, idx, T, k, E, n_shared, c->cnt,
+               c->list, c->max_tokens, c->active, c->n_active, mt, tl, c->n_tiles, x, rows, K,
+               c->mx_hi, c->mx_lo, c->mx_ehi, c->mx_elo);
+    else
+        launch(mx_prep_small_kernel<false>, grid, 1024, 0, st, idx, T, k, E, n_shared, c->cnt,
+               c->list, c->max_tokens, c->active, c->n_active, mt, tl, c->n_tiles, x, rows, K,
+               c->mx_hi, c->mx_lo, c->mx_ehi, c->mx_elo);
+    return hipGetLastError();
+}
+
 static int grid8(int n)
 {
     return (n + 7) & ~7;
@@ -396,10 +451,21 @@ moe_status mx_ffn_enqueue(moe_ctx *c, const void *x, int T, const moe_layer_weig
             return hip_fail(e, what);               \
         prof_end(c, (kind), st);                    \
     } while (0)
-    MX_LAUNCH(MOE_PROF_PERMUTE, "permute launch",
-              launch_permute(idx, T, k, E, d.n_shared, c->cnt, c->list, c->max_tokens, c->active,
-                             c->n_active, c->done, st));
-    MX_LAUNCH(MOE_PROF_TILES, "tile list launch", launch_row_tiles(c, MX_MT, st));
+    const bool mxmma = c->path != MOE_PATH_MX_BF16;
+    // at most 256 routing entries: permutation, tile list and the tokens'
+    // split in one launch
+    const bool prep = T * k <= 256 && E + d.n_shared <= 1024;
+    if (prep) {
+        MX_LAUNCH(MOE_PROF_PERMUTE, "permute/tiles/split launch",
+                  launch_mx_prep_small(idx, T, k, E, d.n_shared, c, MX_MT,
+                                       mxmma ? static_cast<const uint16_t *>(x) : nullptr,
+                                       mxmma ? T : 0, H, st));
+    } else {
+        MX_LAUNCH(MOE_PROF_PERMUTE, "permute launch",
+                  launch_permute(idx, T, k, E, d.n_shared, c->cnt, c->list, c->max_tokens,
+                                 c->active, c->n_active, c->done, st));
+        MX_LAUNCH(MOE_PROF_TILES, "tile list launch", launch_row_tiles(c, MX_MT, st));
+    }
     const int mt_max = (T * c->S + MX_MT - 1) / MX_MT + ((T * k < E ? T * k : E) + d.n_shared);
 
     MxArgs a{};
@@ -414,9 +480,8 @@ moe_status mx_ffn_enqueue(moe_ctx *c, const void *x, int T, const moe_layer_weig
     a.rt.S = c->S;
     const int2 *tl = reinterpret_cast<const int2 *>(c->tiles);
 
-    const bool mxmma = c->path != MOE_PATH_MX_BF16;
     // the tokens' bf16 rows split into E4M3 hi/lo parts with E8M0 scales
-    if (mxmma)
+    if (mxmma && !prep)
         MX_LAUNCH(MOE_PROF_QUANT, "split launch",
                   launch_split_fp8(static_cast<const uint16_t *>(x), T, H, c->mx_hi, c->mx_lo,
                                    c->mx_ehi, c->mx_elo, st));
