@@ -199,10 +199,6 @@ __global__ __launch_bounds__(512, 2) void mfma_proj_kernel(ProjArgs a, const int
         s_row[tid] = row;
         s_sc[tid] = sc;
     }
-    if (tid < NT) {
-        s_emin[tid] = 99;
-        s_emax[tid] = -99;
-    }
     if (tid < 8) {
         // blob tile of LDS weight rows [16*tid, 16*tid+16)
         int t;
@@ -220,30 +216,6 @@ __global__ __launch_bounds__(512, 2) void mfma_proj_kernel(ProjArgs a, const int
         reinterpret_cast<const uint8_t *>((e == a.ex.E) ? a.ex.shared : a.ex.ptrs[e]);
     const int K = a.K, KC = K >> 5, n_stages = KC / KS, G = KC / GS;
     const uint8_t *qbase = reinterpret_cast<const uint8_t *>(a.q);
-
-    // exponent range of each weight row's nonzero scales ([tile][group][r]
-    // layout: thread = (tile, row r, group phase j0), groups j0, j0+4, ...)
-    {
-        const int tj = tid >> 6, r = tid & 15;
-        const uint16_t *sp =
-            reinterpret_cast<const uint16_t *>(blob + a.s_off + (size_t)s_tile[tj] * a.tile_s) + r;
-        int lo = 99, hi = -99;
-        for (int j = (tid >> 4) & 3; j < G; j += 4) {
-            const uint16_t h = sp[(size_t)j * 16];
-            if (h & 0x7fff) {
-                const int ef = (h >> 10) & 31;
-                const int ev = ef ? ef : 1;
-                lo = min(lo, ev);
-                hi = max(hi, ev);
-            }
-        }
-        atomicMin(&s_emin[16 * tj + r], lo);
-        atomicMax(&s_emax[16 * tj + r], hi);
-    }
-    __syncthreads();
-    const int wide_row =
-        (tid < NT && s_emax[tid] - s_emin[tid] > MAX_INT_SPREAD) ? 1 : 0;   // all-zero rows: -198
-    const bool wide = __syncthreads_or(wide_row) != 0;
 
     // global -> LDS per stage, one piece of each kind per thread: activations
     // 64 rows x 8 pieces of 16 B; weight nibbles 8 tiles x 4 chunks x 16 rows
@@ -268,14 +240,13 @@ __global__ __launch_bounds__(512, 2) void mfma_proj_kernel(ProjArgs a, const int
     constexpr int NG = KS / GS;
     const bool s_thread = tid < NT * NG;
     const uint16_t *gs_;
-    int ls_, em_;
+    int ls_;
     {
         const int sq = s_thread ? tid : 0;
         const int row = sq / NG, u = sq % NG;
         gs_ = reinterpret_cast<const uint16_t *>(blob + a.s_off + (size_t)s_tile[row >> 4] * a.tile_s) +
               u * 16 + (row & 15);
         ls_ = row * KS + u;
-        em_ = s_emin[row];
     }
 
     const int wave = tid >> 6, lane = tid & 63;
@@ -344,8 +315,6 @@ __global__ __launch_bounds__(512, 2) void mfma_proj_kernel(ProjArgs a, const int
     } while (0)
 #define KLOOP(INTM, EPI)                                                          \
     do {                                                                          \
-        GLOAD(0, 0);                                                              \
-        GLOAD(1, 1);                                                              \
         LSTORE(0, 0, INTM);                                                       \
         __syncthreads();                                                          \
         for (int st = 0; st < n_stages; st += 2) {                                \
@@ -353,6 +322,72 @@ __global__ __launch_bounds__(512, 2) void mfma_proj_kernel(ProjArgs a, const int
             KSTAGE(1, 0, st + 1, INTM, EPI);                                      \
         }                                                                         \
     } while (0)
+
+    // Exponent range of each weight row's nonzero scales.  The scales of a
+    // tile are [group][16 rows] (fp16): wave w reads tile w, lane l the rows
+    // [8(l>>5), 8(l>>5)+8) of groups (l&31) + 32i, 16 bytes per load, a batch
+    // of SCAN_LOADS loads in flight at once (the first batch also beside the
+    // first two stages' loads, which go out right after it); each lane marks
+    // the exponents it sees per row in a 32-bit set (subnormals count as
+    // exponent 1), the sets are OR-ed over the 32 lanes of each half-wave, and
+    // the lowest and highest member are the row's Emin and Emax (99 and -99
+    // for a row of zero scales).
+    {
+        constexpr int SCAN_LOADS = 8;
+        const int hf = lane >> 5, p = lane & 31;
+        const uint4 *sp = reinterpret_cast<const uint4 *>(blob + a.s_off +
+                                                          (size_t)s_tile[wave] * a.tile_s) + hf;
+        uint32_t eset[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        uint4 v[SCAN_LOADS];
+        // groups past G load a valid group and are ignored
+#define SCAN_ISSUE(b)                                                             \
+        _Pragma("unroll") for (int i = 0; i < SCAN_LOADS; ++i)                    \
+            v[i] = sp[2 * min((b) + 32 * i + p, G - 1)]
+#define SCAN_MARK(b)                                                              \
+        _Pragma("unroll") for (int i = 0; i < SCAN_LOADS; ++i) {                  \
+            const bool ok_ = (b) + 32 * i + p < G;                                \
+            const uint32_t wd_[4] = {v[i].x, v[i].y, v[i].z, v[i].w};             \
+            _Pragma("unroll") for (int q = 0; q < 8; ++q) {                       \
+                const uint32_t h_ = (wd_[q >> 1] >> (16 * (q & 1))) & 0xffffu;   \
+                const uint32_t ef_ = (h_ >> 10) & 31u;                            \
+                eset[q] |= (ok_ && (h_ & 0x7fffu)) ? (1u << (ef_ ? ef_ : 1u)) : 0u; \
+            }                                                                     \
+        }
+        SCAN_ISSUE(0);
+        GLOAD(0, 0);
+        GLOAD(1, 1);
+        __builtin_amdgcn_sched_barrier(0);      // keep those loads ahead of the marking
+        SCAN_MARK(0);
+        for (int b = 32 * SCAN_LOADS; b < G; b += 32 * SCAN_LOADS) {
+            SCAN_ISSUE(b);
+            SCAN_MARK(b);
+        }
+#undef SCAN_ISSUE
+#undef SCAN_MARK
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            uint32_t m = eset[q];
+            m |= (uint32_t)xor_lane<1>((int)m);
+            m |= (uint32_t)xor_lane<2>((int)m);
+            m |= (uint32_t)xor_lane<4>((int)m);
+            m |= (uint32_t)xor_lane<8>((int)m);
+            m |= (uint32_t)xor_lane<16>((int)m);
+            eset[q] = m;
+        }
+        if (p == 0) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int row = 16 * wave + 8 * hf + q;
+                s_emin[row] = eset[q] ? __builtin_ctz(eset[q]) : 99;
+                s_emax[row] = eset[q] ? 31 - __builtin_clz(eset[q]) : -99;
+            }
+        }
+    }
+    __syncthreads();
+    const int wide_row =
+        (tid < NT && s_emax[tid] - s_emin[tid] > MAX_INT_SPREAD) ? 1 : 0;   // all-zero rows: -198
+    const bool wide = __syncthreads_or(wide_row) != 0;
+    const int em_ = s_emin[(s_thread ? tid : 0) / NG];
 
     double acc[16];
     if (!wide) {
