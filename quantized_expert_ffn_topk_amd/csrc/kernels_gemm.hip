@@ -339,12 +339,16 @@ __global__ __launch_bounds__(512, 2) void mfma_proj_kernel(ProjArgs a, const int
                                                           (size_t)s_tile[wave] * a.tile_s) + hf;
         uint32_t eset[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
         uint4 v[SCAN_LOADS];
-        // groups past G load a valid group and are ignored
+        // (a batch issues only the loads whose groups start below G; lanes
+        // whose group is past G load a valid group and ignore it)
 #define SCAN_ISSUE(b)                                                             \
         _Pragma("unroll") for (int i = 0; i < SCAN_LOADS; ++i)                    \
-            v[i] = sp[2 * min((b) + 32 * i + p, G - 1)]
+            if ((b) + 32 * i < G)                                                 \
+                v[i] = sp[2 * min((b) + 32 * i + p, G - 1)]
 #define SCAN_MARK(b)                                                              \
         _Pragma("unroll") for (int i = 0; i < SCAN_LOADS; ++i) {                  \
+            if ((b) + 32 * i >= G)                                                \
+                break;                                                            \
             const bool ok_ = (b) + 32 * i + p < G;                                \
             const uint32_t wd_[4] = {v[i].x, v[i].y, v[i].z, v[i].w};             \
             _Pragma("unroll") for (int q = 0; q < 8; ++q) {                       \
