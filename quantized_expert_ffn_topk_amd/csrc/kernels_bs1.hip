@@ -660,13 +660,14 @@ __global__ __launch_bounds__(64 * 12) void down_bs1h_kernel(Bs1Args a)
     int8_t *lq = reinterpret_cast<int8_t *>(smem) + (size_t)ai * F;
 
     float sc = 0.0f;
-    // the combine's ids and weights, fetched while the weights stream
+    // the combine's ids and weights: loaded here (every thread, so that no
+    // wave waits for them before its own loads) and written to LDS before the
+    // block's barrier
     __shared__ float s_w[16];
     __shared__ int s_e[16];
-    if (threadIdx.x < a.k) {
-        s_e[threadIdx.x] = a.idx[threadIdx.x];
-        s_w[threadIdx.x] = a.w[threadIdx.x];
-    }
+    const int cw = threadIdx.x < a.k ? threadIdx.x : 0;
+    const int e_cw = a.idx[cw];
+    const float w_cw = a.w[cw];
     const float4 *hr = reinterpret_cast<const float4 *>(a.h + (size_t)ai * F);
     float4 hv[8];
 #pragma unroll
@@ -736,6 +737,10 @@ __global__ __launch_bounds__(64 * 12) void down_bs1h_kernel(Bs1Args a)
                 a.Y[(size_t)ai * a.H + 8 * NH * pr + 8 * i + r] = y;
             }
         }
+    }
+    if (threadIdx.x < a.k) {
+        s_e[threadIdx.x] = e_cw;
+        s_w[threadIdx.x] = w_cw;
     }
     __syncthreads();
     if (threadIdx.x < 8 * NH) {

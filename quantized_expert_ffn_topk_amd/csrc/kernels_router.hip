@@ -718,22 +718,33 @@ __global__ __launch_bounds__(256) void route_small_kernel(RouteSmallArgs a)
     uint2 xq_v[8];                       // this block's share of token 0 (T == 1)
     if (a.flags & RS_ROUTER) {
         const int e = blockIdx.x;
-        // all of this thread's router-row loads first (H <= 8192), then the FMAs
+        // all of this thread's router-row loads first (H <= 8192), then the
+        // FMAs; lanes past H read the row's first inputs and zero them after
+        // the loads (a load under the branch let the compiler convert each
+        // value as it arrived, one round trip at a time)
         constexpr int NI = 8;
         float4 wv[NI];
         const float *wr = a.Wr + (size_t)e * a.H;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int k0 = tid * 4 + 1024 * i;
-            wv[i] = (k0 < a.H) ? *reinterpret_cast<const float4 *>(wr + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
+            wv[i] = *reinterpret_cast<const float4 *>(wr + ((k0 < a.H) ? k0 : 0));
         }
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            if (tid * 4 + 1024 * i >= a.H)
+                wv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int m = 0; m < T; ++m) {
             uint2 xv[NI];
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 const int k0 = tid * 4 + 1024 * i;
-                xv[i] = (k0 < a.H) ? *reinterpret_cast<const uint2 *>(a.x + (size_t)m * a.H + k0) : make_uint2(0u, 0u);
+                xv[i] = *reinterpret_cast<const uint2 *>(a.x + (size_t)m * a.H + ((k0 < a.H) ? k0 : 0));
             }
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+                if (tid * 4 + 1024 * i >= a.H)
+                    xv[i] = make_uint2(0u, 0u);
             double acc = 0.0;
             float amax = 0.0f;
 #pragma unroll
@@ -905,11 +916,22 @@ __global__ __launch_bounds__(256) void router_bs1_kernel(RouteSmallArgs a)
     float4 wv[NI];
     uint2 xv[NI];
     const float *wr = a.Wr + (size_t)e * a.H;
+    // every load is issued before any is used: lanes past H read the row's
+    // first inputs and zero them afterwards (a load under the branch let the
+    // compiler convert each value as it arrived, one round trip at a time)
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int k0 = tid * 4 + 1024 * i;
-        wv[i] = (k0 < a.H) ? *reinterpret_cast<const float4 *>(wr + k0) : make_float4(0.f, 0.f, 0.f, 0.f);
-        xv[i] = (k0 < a.H) ? *reinterpret_cast<const uint2 *>(a.x + k0) : make_uint2(0u, 0u);
+        const int kc = (k0 < a.H) ? k0 : 0;
+        wv[i] = *reinterpret_cast<const float4 *>(wr + kc);
+        xv[i] = *reinterpret_cast<const uint2 *>(a.x + kc);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        if (tid * 4 + 1024 * i >= a.H) {
+            wv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            xv[i] = make_uint2(0u, 0u);
+        }
     }
     double acc = 0.0;
     float amax = 0.0f;
