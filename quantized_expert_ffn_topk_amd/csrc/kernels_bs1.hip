@@ -213,12 +213,15 @@ __global__ __launch_bounds__(256) void topk_bs1_kernel(const double *__restrict_
     double c = -INFINITY;
     int ci = INT_MAX;
     if (tid < E) {
-        if (ptrs)
-            s_ptr[tid] = ptrs[tid];
+        // the blob pointer's load goes out with the score's loads and is
+        // stored after them, so the two share one round trip
+        const void *pt = ptrs ? ptrs[tid] : nullptr;
         double sv;
         c = bs1_scores(logits, bias, tid, sv);
         s_s[tid] = sv;
         ci = tid;
+        if (ptrs)
+            s_ptr[tid] = pt;
     }
     topk_select_256(c, ci, s_s, a.k, r, idx_out, w_out, s_idx, cand_c, cand_i, sel_s);
     if (ptrs && tid < a.k)
@@ -324,12 +327,15 @@ __global__ __launch_bounds__(512) void topk_bs1h_kernel(const double *__restrict
     double c = -INFINITY;
     int ci = INT_MAX;
     if (tid < E) {
-        if (ptrs)
-            s_ptr[tid] = ptrs[tid];
+        // the blob pointer's load goes out with the score's loads and is
+        // stored after them, so the two share one round trip
+        const void *pt = ptrs ? ptrs[tid] : nullptr;
         double sv;
         c = bs1_scores(logits, bias, tid, sv);
         s_s[tid] = sv;
         ci = tid;
+        if (ptrs)
+            s_ptr[tid] = pt;
     }
     topk_select_256(c, ci, s_s, a.k, r, idx_out, w_out, s_idx, cand_c, cand_i, sel_s);
     if (ptrs && tid < a.k)

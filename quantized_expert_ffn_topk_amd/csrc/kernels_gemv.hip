@@ -39,7 +39,7 @@ template <int U, bool CACHED>
 __device__ __forceinline__ void load_batch(const uint8_t *__restrict__ wt,
                                            const uint16_t *__restrict__ st, int cb, int it0,
                                            int niter, int c4, int r, int gshift,
-                                           uint4 (&wv)[U], uint16_t (&sv)[U])
+                                           uint4 (&wv)[U], uint32_t (&sv)[U])
 {
     typedef unsigned int g4 __attribute__((ext_vector_type(4)));
     if constexpr (CACHED) {
@@ -65,7 +65,7 @@ __device__ __forceinline__ void load_batch(const uint8_t *__restrict__ wt,
 }
 
 template <int MG, int U>
-__device__ __forceinline__ void compute_batch(const uint4 (&wv)[U], const uint16_t (&sv)[U], int cb,
+__device__ __forceinline__ void compute_batch(const uint4 (&wv)[U], const uint32_t (&sv)[U], int cb,
                                               int it0, int niter, int c4, int mc,
                                               const int8_t *__restrict__ lq, int K, double (&p)[MG])
 {
@@ -73,7 +73,7 @@ __device__ __forceinline__ void compute_batch(const uint4 (&wv)[U], const uint16
     for (int u = 0; u < U; ++u) {
         if (it0 + u < niter) {
             const int c = cb + (it0 + u) * 4 + c4;
-            const double sd = (double)f16_to_f32(sv[u]) * 0.0625;
+            const double sd = (double)f16_to_f32((uint16_t)sv[u]) * 0.0625;
             const uint32_t wd[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
             int lo[4], hi[4];
 #pragma unroll
@@ -185,7 +185,8 @@ __device__ __forceinline__ void gemv_tile_pair(const ProjArgs &a, const uint8_t 
     const int niter = nk >> 2;
 
     uint4 wv[U];
-    uint16_t sv[U];
+    uint32_t sv[U];           // 16-bit scales, one per register: packing two per
+                              // register made each load wait for the one before
     load_batch<U, CACHED>(wt, st, cb, 0, niter, c4, r, a.group_shift, wv, sv);   // before staging
     for (int base = 0; base < n; base += MG) {
         const int mc = min(MG, n - base);
