@@ -141,24 +141,62 @@ __device__ __forceinline__ void requant_row_dev(const float *__restrict__ hr, in
         *s_out = sc;
 }
 
-// Stages up to MG activation rows of the expert's list into LDS.
+// Stages up to MG activation rows of the expert's list into LDS: the pass's
+// slots first (one load per row, all rows at once), then the rows' codes,
+// copied global -> LDS by the load unit (global_load_lds_dwordx4: a wave moves
+// 1 KiB, lane l's 16 bytes to LDS byte 16 l of the wave's destination) with
+// every copy of the pass in flight at once, and the rows' token scales beside
+// them: two round trips for the pass, where one row at a time took two per
+// row.  Rows whose length is not a multiple of 1 KiB take plain copies.  The
+// caller's next barrier publishes lq, lsa and lslot.
 template <int MG>
 __device__ __forceinline__ void stage_rows(const ProjArgs &a, const int32_t *lst, int base,
                                            int mc, int8_t *lq, float *lsa, int *lslot)
 {
     const int K = a.K;
-    for (int m = 0; m < mc; ++m) {
-        const int slot = lst[base + m];
-        const int row = a.in_by_token ? slot / a.rt.S : slot;
-        const uint4 *src = reinterpret_cast<const uint4 *>(a.q + (size_t)row * K);
-        uint4 *dst = reinterpret_cast<uint4 *>(lq + m * K);
-        for (int i = threadIdx.x; i < K / 16; i += 256)
-            dst[i] = src[i];
-        if (threadIdx.x == 0)
-            lsa[m] = a.s[row];
-        if (threadIdx.x == 0)
-            lslot[m] = slot;
+    const int tid = threadIdx.x;
+    if (tid < mc)
+        lslot[tid] = lst[base + tid];
+    __syncthreads();
+    float sc = 0.0f;
+    if (tid < mc) {
+        const int slot = lslot[tid];
+        sc = a.s[a.in_by_token ? slot / a.rt.S : slot];
     }
+    if ((K & 1023) == 0) {
+        const int gpr = K >> 10;                     // 1 KiB pieces per row
+        const int wave = tid >> 6, lane = tid & 63;
+        int m = 0, g = wave;
+        while (m < mc && g >= gpr) {
+            g -= gpr;
+            ++m;
+        }
+        for (; m < mc;) {
+            const int slot = lslot[m];
+            const int row = a.in_by_token ? slot / a.rt.S : slot;
+            const int8_t *src = a.q + (size_t)row * K + 1024 * g + 16 * lane;
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)src,
+                (__attribute__((address_space(3))) void *)(lq + (size_t)m * K + 1024 * g), 16, 0, 0);
+            g += 4;
+            while (m < mc && g >= gpr) {
+                g -= gpr;
+                ++m;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0f70);          // vmcnt(0): the copies have landed
+    } else {
+        for (int m = 0; m < mc; ++m) {
+            const int slot = lslot[m];
+            const int row = a.in_by_token ? slot / a.rt.S : slot;
+            const uint4 *src = reinterpret_cast<const uint4 *>(a.q + (size_t)row * K);
+            uint4 *dst = reinterpret_cast<uint4 *>(lq + m * K);
+            for (int i = tid; i < (K >> 4); i += 256)
+                dst[i] = src[i];
+        }
+    }
+    if (tid < mc)
+        lsa[tid] = sc;
 }
 
 // Exact partial sums of tile pair (wt0, wt1) for all passes of MG rows; calls
